@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""FP32 SGEMM benchmark on one MI355X: TFLOPS = 2MNK/t at NN 4096^3.
+
+One step is one mi_sgemm call on the headline workload (row-major NN,
+M = N = K = 4096, alpha = 1, beta = 0, A and B uniform [-1, 1) from
+srand48(4)); inputs are resident in HBM before timing starts. The FLOP
+count 2MNK is the convention of the klklkl10086.github.io SGEMM page
+(problem definition), where 4096^3 is 137.4 GFLOP.
+
+Prints one JSON line. Besides the contract fields it carries
+  roofline      the SGEMM kernel against the FP32 matrix-core peak, with the
+                average launch time measured by HIP events on the launch stream,
+                and HBM traffic from the committed rocprofv3 counter summary
+                when that summary was taken on the current kernel source;
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample.
+
+Other modes: --table writes per-workload TFLOPS (and GB/s for the skinny
+product) to a JSON-lines file; --mode copy runs a plain device copy of known
+size, used to calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SGEMM TFLOPS (2MNK/t) at 4096^3 and % of MI355X FP32 matrix peak"
+PEAK_FP32_MATRIX_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 FLOP/clk/CU
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "fp32_gemm_nn_amd", "csrc", "misgemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_nn_4096.json")
+COPY_BYTES = 256 << 20
+
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    return 2 * M * N * K
+
+
+def tflops(flops: float, seconds: float) -> float:
+    return flops / seconds / 1e12
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(launch_flops_case):
+    """HBM bytes per launch from the committed counter summary, or None if it
+    is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash() or t.get("workload") != launch_flops_case:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+class Problem:
+    """Device buffers for one workload, optionally several independent copies."""
+
+    def __init__(self, case, copies=1):
+        import torch
+        from synthetic import workloads as W
+
+        self.case = case
+        inp = W.make_inputs(case)
+        self.sets = []
+        for i in range(copies):
+            A = torch.from_numpy(inp.A).cuda()
+            B = torch.from_numpy(inp.B).cuda()
+            C = torch.from_numpy(inp.C.copy()).cuda()
+            self.sets.append((A, B, C))
+        torch.cuda.synchronize()
+
+    def call(self, i=0, stream=None):
+        import fp32_gemm_nn_amd as mg
+
+        c = self.case
+        A, B, C = self.sets[i % len(self.sets)]
+        rc = mg.mi_sgemm(c.transA, c.transB, c.M, c.N, c.K, c.alpha, A.data_ptr(), c.lda_,
+                         B.data_ptr(), c.ldb_, c.beta, C.data_ptr(), c.ldc_, stream)
+        if rc != 0:
+            raise RuntimeError(f"mi_sgemm: {mg.mi_sgemm_status_string(rc)}")
+
+
+def time_problem(prob, steps, warmup):
+    """Wall time and HIP-event time of `steps` back-to-back calls on one stream."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    for i in range(warmup):
+        prob.call(i, handle)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        prob.call(i, handle)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1) / 1e3
+
+
+def cpu_baseline(case, min_seconds=10.0, max_seconds=30.0):
+    """Time the CPU oracle (as it stands) on the headline product.
+
+    The sample is whole products of the headline workload, repeated until at
+    least `min_seconds` have passed; if one product would exceed `max_seconds`
+    (estimated from a 64-row slice), a leading block of rows is used instead.
+    """
+    import numpy as np
+
+    import oracle
+    from synthetic import workloads as W
+
+    inp = W.make_inputs(case)
+    threads = oracle.num_threads()
+    # Estimate from a small slice of rows.
+    rows = 64
+    C = np.zeros((rows, case.N), np.float32)
+    t0 = time.perf_counter()
+    oracle.sgemm(case.transA, case.transB, rows, case.N, case.K, case.alpha, inp.A, case.lda_, inp.B,
+                 case.ldb_, case.beta, C, case.ldc_)
+    est_full = (time.perf_counter() - t0) * case.M / rows
+    if est_full > max_seconds:
+        rows = max(64, int(case.M * max_seconds / est_full / 2))
+    else:
+        rows = case.M
+    C = np.zeros((rows, case.N), np.float32)
+    reps, spent = 0, 0.0
+    while spent < min_seconds and (reps == 0 or spent + spent / reps <= max_seconds):
+        t0 = time.perf_counter()
+        rc = oracle.sgemm(case.transA, case.transB, rows, case.N, case.K, case.alpha, inp.A, case.lda_,
+                          inp.B, case.ldb_, case.beta, C, case.ldc_)
+        spent += time.perf_counter() - t0
+        assert rc == 0
+        reps += 1
+    flops = gemm_flops(rows, case.N, case.K) * reps
+    sample = (f"{reps} x full {case.M}x{case.N}x{case.K} {case.transA}{case.transB} product"
+              if rows == case.M else
+              f"{reps} x first {rows} rows of the {case.M}x{case.N}x{case.K} {case.transA}{case.transB} product")
+    return {"value": round(tflops(flops, spent), 6), "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle", "sample": sample, "seconds": round(spent, 2)}
+
+
+def host_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def run_copy(steps, warmup):
+    """A plain device copy of COPY_BYTES per launch (counter calibration)."""
+    import torch
+
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": COPY_BYTES, "bytes_written_per_launch": COPY_BYTES,
+                      "steps": steps, "GBps": round(2 * COPY_BYTES * steps / dt / 1e9, 1)}))
+
+
+def run_table(path, steps, warmup):
+    """Per-workload TFLOPS for every configuration (one JSON object per line)."""
+    import fp32_gemm_nn_amd as mg
+    from synthetic import workloads as W
+
+    cases = [W.C1, W.C2, *[W.c3(n) for n in W.C3_SIZES], W.C4, *W.C5A, W.C5B]
+    with open(path, "w") as out:
+        for case in cases:
+            skinny = case is W.C5B
+            # The skinny product streams 64 MiB of B; rotate 8 independent
+            # operand sets (> 512 MiB) so repeated calls do not hit in the
+            # 256 MB last-level cache.
+            prob = Problem(case, copies=8 if skinny else 1)
+            n = max(steps, int(2e-1 / max(case.flops / 100e12, 1e-6))) if not skinny else max(steps, 200)
+            n = min(n, 2000)
+            _, ev = time_problem(prob, n, warmup)
+            per = ev / n
+            row = {"workload": case.name, "transA": case.transA, "transB": case.transB, "M": case.M,
+                   "N": case.N, "K": case.K, "alpha": case.alpha, "beta": case.beta,
+                   "kernel_config": mg.mi_sgemm_config_name(
+                       mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)),
+                   "us_per_call": round(per * 1e6, 3), "TFLOPS": round(tflops(case.flops, per), 3),
+                   "pct_fp32_matrix_peak": round(100 * tflops(case.flops, per) / PEAK_FP32_MATRIX_TFLOPS, 2),
+                   "GBps_algorithmic": round(case.algorithmic_bytes / per / 1e9, 1)}
+            if skinny:
+                row["pct_hbm_peak"] = round(100 * case.algorithmic_bytes / per / 1e9 / PEAK_HBM_GBPS, 2)
+            out.write(json.dumps(row) + "\n")
+            out.flush()
+            print(json.dumps(row), file=sys.stderr, flush=True)
+            del prob
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--mode", choices=["gemm", "copy"], default="gemm")
+    ap.add_argument("--table", metavar="PATH", help="also write per-workload numbers to PATH")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this SGEMM runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp32_gemm_nn_amd as mg
+    from synthetic import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mg.load_library()
+
+    if args.mode == "copy":
+        run_copy(args.steps, args.warmup)
+        return
+
+    case = W.HEADLINE
+    prob = Problem(case)
+    wall, ev = time_problem(prob, args.steps, args.warmup)
+    flops = case.flops
+    value = tflops(flops * args.steps, wall)
+    per_launch = ev / args.steps
+    achieved = tflops(flops, per_launch)
+    traffic = load_traffic(case.name)
+    cfg_id = mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"sgemm_{case.transA}{case.transB}_{case.M}x{case.N}x{case.K}".lower(),
+            "M": case.M, "N": case.N, "K": case.K, "transA": case.transA, "transB": case.transB,
+            "alpha": case.alpha, "beta": case.beta, "inputs": "uniform [-1,1) from srand48(4)",
+            "kernel_config": mg.mi_sgemm_config_name(cfg_id),
+            "pct_fp32_matrix_peak": round(100 * value / PEAK_FP32_MATRIX_TFLOPS, 2),
+            "gpu": torch.cuda.get_device_name(0),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_FP32_MATRIX_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_us_per_launch": round(per_launch * 1e6, 2),
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": case.algorithmic_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    del prob
+    if args.table:
+        run_table(args.table, 20, 5)
+    if not args.no_cpu:
+        cb = cpu_baseline(case)
+        cb.update(host_info())
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,540 @@
+// misgemm -- FP32 SGEMM on CDNA4 (gfx950) matrix cores, behind a C ABI.
+//
+// C = alpha*op(A)*op(B) + beta*C, row-major, op in {N, T}: the BLAS SGEMM of
+// the itan.pw RTX 4090 SGEMM page (overview), with the row-major sum of the
+// problem definition of "【CUDA】Sgemm单精度矩阵乘法" (klklkl10086.github.io).
+//
+// Kernel shape (one workgroup per BM x BN tile of C):
+//   * The k range is walked in BK-wide tiles. Each tile of op(A) (BM x BK) and
+//     op(B) (BK x BN) is fetched with 16-byte global loads along whichever
+//     axis is contiguous in memory and stored unchanged into one of two LDS
+//     buffers, so one barrier per k-tile suffices (the double buffering of the
+//     itan.pw page, sections 3.6-3.7: the write-after-read barrier goes away
+//     when consecutive tiles live in different buffers). The next tile's
+//     global loads are issued before the current tile's matrix instructions.
+//   * Each wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of C held in
+//     accumulator registers as FM x FN blocks of 32 x 32 (the register tile of
+//     the same page, section 3.4, moved onto the matrix cores), and issues
+//     v_mfma_f32_32x32x2_f32: full FP32 inputs, products and sums.
+//   * k-permutation: inside a k-tile, the two 32-lane halves of a wave feed the
+//     MFMA's two k slots from the two halves of the tile (slot h of step s is
+//     k = h*BK/2 + s). Any permutation of k applied to both operands only
+//     reorders the sum, and this one makes each lane's successive k values
+//     adjacent, so one ds_read_b128 feeds four MFMAs from a k-contiguous LDS
+//     tile -- the role played by the transposed A tile of section 3.5.
+//   * Operands whose contiguous axis is m or n (A transposed, B not
+//     transposed) stay m/n-contiguous in LDS. For those, MFMA block b of a wave
+//     takes columns FN*c + b (c = lane column), so one ds_read of FN adjacent
+//     floats serves all FN blocks at once, and each lane ends up holding FN
+//     adjacent outputs of a row, which the epilogue stores as one vector.
+//   * LDS rows are padded by 4 floats (the padding remedy of section 3.8); the
+//     16-byte reads of the k-contiguous tiles are then bank-conflict free.
+//   * Edges: a workgroup whose tile, or whose current k-tile, crosses M, N or
+//     K takes a guarded load path that reads only in-range elements and
+//     selects zero for the rest (the zero-fill of the klklkl10086 page,
+//     01-Shared Memory Tiling); stores are masked to i < M, j < N.
+//   * Epilogue: C = alpha*acc + beta*C fused into the store (itan.pw page,
+//     sections 3.4-3.5); when beta == 0, C is not read.
+//   * Workgroup order: consecutive workgroups are dealt round-robin to the 8
+//     XCDs, each with its own L2. The launch index is remapped so each XCD
+//     receives one contiguous run of tiles, walked in column groups of
+//     GROUP_M tile rows, so tiles sharing A rows and B columns meet in the
+//     same L2.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "misgemm.h"
+
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+constexpr int kLdsPad = 4;
+
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int M, N, K;
+    int lda, ldb, ldc;
+    float alpha, beta;
+    int tiles_m, tiles_n;
+    int vec_ab;   // A and B: 16-byte aligned base, lda and ldb multiples of 4
+    int vec_c;    // C: 16-byte aligned base, ldc multiple of 4
+};
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+};
+
+// n adjacent floats from LDS (n = 1, 2, 4), as one ds_read.
+template <int n> struct LdsVec;
+template <> struct LdsVec<1> {
+    static __device__ __forceinline__ void get(const float *p, float *out) { out[0] = *p; }
+};
+template <> struct LdsVec<2> {
+    static __device__ __forceinline__ void get(const float *p, float *out) {
+        f32x2 v = *reinterpret_cast<const f32x2 *>(p);
+        out[0] = v[0]; out[1] = v[1];
+    }
+};
+template <> struct LdsVec<4> {
+    static __device__ __forceinline__ void get(const float *p, float *out) {
+        f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    }
+};
+
+// One R x CC tile of a stored row-major matrix, moved global -> registers ->
+// LDS in 16-byte chunks. Thread t handles chunks t, t+NT, ...; a chunk is four
+// consecutive columns of one row. LDS layout: [R][CC + kLdsPad].
+template <int R, int CC, int NT>
+struct TileCopy {
+    static constexpr int CPR = CC / 4;                  // chunks per row
+    static constexpr int CHUNKS = R * CPR;
+    static constexpr int PER_THREAD = CHUNKS / NT;
+    static constexpr int STRIDE = CC + kLdsPad;
+    static constexpr int LDS_FLOATS = R * STRIDE;
+    static_assert(CC % 4 == 0 && CHUNKS % NT == 0, "tile must split evenly over the threads");
+
+    f32x4 v[PER_THREAD];
+
+    // base points at stored element (r0, c0); rows_left / cols_left count the
+    // in-range rows and columns from there (may exceed R / CC).
+    __device__ __forceinline__ void load(const float *__restrict__ base, int ld, int rows_left,
+                                         int cols_left, bool guard, bool vec, int tid) {
+        if (!guard) {
+#pragma unroll
+            for (int j = 0; j < PER_THREAD; ++j) {
+                const int idx = tid + NT * j;
+                const int r = idx / CPR, c = (idx % CPR) * 4;
+                v[j] = *reinterpret_cast<const f32x4 *>(base + (size_t)r * ld + c);
+            }
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int idx = tid + NT * j;
+            const int r = idx / CPR, c = (idx % CPR) * 4;
+            const float *p = base + (size_t)r * ld + c;
+            if (vec && r < rows_left && c + 3 < cols_left) {
+                v[j] = *reinterpret_cast<const f32x4 *>(p);
+            } else {
+                f32x4 t;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    t[e] = (r < rows_left && c + e < cols_left) ? p[e] : 0.0f;
+                v[j] = t;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(float *lds, int tid) const {
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int idx = tid + NT * j;
+            const int r = idx / CPR, c = (idx % CPR) * 4;
+            *reinterpret_cast<f32x4 *>(lds + r * STRIDE + c) = v[j];
+        }
+    }
+};
+
+// Launch index -> (tile row, tile column). Workgroup b runs on XCD b % 8; the
+// j-th workgroup of XCD x is given logical tile prefix(x) + j, so each XCD
+// walks one contiguous run of logical tiles. Logical tiles are ordered in
+// groups of kGroupM tile rows, column by column within a group.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int bid = blockIdx.x;
+    const int total = gridDim.x;
+    const int q = total / kXcds, rem = total % kXcds;
+    const int x = bid % kXcds, j = bid / kXcds;
+    const int logical = x * q + (x < rem ? x : rem) + j;
+    const int per_group = kGroupM * tiles_n;
+    const int group = logical / per_group;
+    const int first_m = group * kGroupM;
+    const int gsz = min(tiles_m - first_m, kGroupM);
+    const int in_g = logical - group * per_group;
+    tm = first_m + in_g % gsz;
+    tn = in_g / gsz;
+}
+
+template <class CFG, bool TA, bool TB>
+__global__ __launch_bounds__(CFG::NT) void sgemm_mfma32(GemmArgs g) {
+    constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NT = CFG::NT;
+    constexpr int FM = CFG::FM, FN = CFG::FN, WTM = CFG::WTM, WTN = CFG::WTN;
+    constexpr int HB = BK / 2;
+    // Stored tile shapes: A is BM x BK ('N', k contiguous) or BK x BM ('T',
+    // m contiguous); B is BK x BN ('N', n contiguous) or BN x BK ('T').
+    using ACopy = TileCopy<TA ? BK : BM, TA ? BM : BK, NT>;
+    using BCopy = TileCopy<TB ? BN : BK, TB ? BK : BN, NT>;
+    constexpr int A_FLOATS = ACopy::LDS_FLOATS, B_FLOATS = BCopy::LDS_FLOATS;
+    constexpr int AS = ACopy::STRIDE, BS = BCopy::STRIDE;
+
+    __shared__ __attribute__((aligned(16))) float lds[2 * (A_FLOATS + B_FLOATS)];
+    // Buffer i of A at lds + i*A_FLOATS, of B at lds + 2*A_FLOATS + i*B_FLOATS.
+    float *const a_lds = lds;
+    float *const b_lds = lds + 2 * A_FLOATS;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 31, lh = lane >> 5;
+    const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
+
+    int tm, tn;
+    tile_coords(g.tiles_m, g.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int M = g.M, N = g.N, K = g.K;
+    const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
+    const bool vec = g.vec_ab != 0;
+
+    // Base of the tile at k = 0 in each stored matrix, and the per-k-tile step.
+    const float *a_ptr = TA ? g.A + m0 : g.A + (size_t)m0 * g.lda;
+    const float *b_ptr = TB ? g.B + (size_t)n0 * g.ldb : g.B + n0;
+    const size_t a_step = TA ? (size_t)BK * g.lda : (size_t)BK;
+    const size_t b_step = TB ? (size_t)BK : (size_t)BK * g.ldb;
+    const int a_rows = TA ? K : M - m0, a_cols = TA ? M - m0 : K;
+    const int b_rows = TB ? N - n0 : K, b_cols = TB ? K : N - n0;
+
+    ACopy ca;
+    BCopy cb;
+    const int ktiles = (K + BK - 1) / BK;
+
+    auto fetch = [&](int kt) {
+        const int k0 = kt * BK;
+        const bool guard = !(full_mn && vec && k0 + BK <= K);
+        // Rows/cols left counted from this k-tile's origin.
+        ca.load(a_ptr + kt * a_step, g.lda, TA ? a_rows - k0 : a_rows, TA ? a_cols : a_cols - k0,
+                guard, vec, tid);
+        cb.load(b_ptr + kt * b_step, g.ldb, TB ? b_rows : b_rows - k0, TB ? b_cols - k0 : b_cols,
+                guard, vec, tid);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    fetch(0);
+    ca.store(a_lds, tid);
+    cb.store(b_lds, tid);
+    __syncthreads();
+
+    for (int kt = 0; kt < ktiles; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < ktiles) fetch(kt + 1);
+
+        const float *as = a_lds + cur * A_FLOATS;
+        const float *bs = b_lds + cur * B_FLOATS;
+#pragma unroll
+        for (int q = 0; q < BK / 8; ++q) {
+            float af[FM][4], bf[FN][4];
+            if (!TA) {
+                // k-contiguous A tile [m][k]: block a, lane row li is m = 32a + li.
+#pragma unroll
+                for (int a = 0; a < FM; ++a) {
+                    const float *p = as + (wm * WTM + 32 * a + li) * AS + lh * HB + 4 * q;
+                    LdsVec<4>::get(p, af[a]);
+                }
+            } else {
+                // m-contiguous A tile [k][m]: block a, lane row li is m = FM*li + a.
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float t[FM];
+                    LdsVec<FM>::get(as + (lh * HB + 4 * q + e) * AS + wm * WTM + FM * li, t);
+#pragma unroll
+                    for (int a = 0; a < FM; ++a) af[a][e] = t[a];
+                }
+            }
+            if (TB) {
+                // k-contiguous B tile [n][k]: block b, lane column li is n = 32b + li.
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const float *p = bs + (wn * WTN + 32 * b + li) * BS + lh * HB + 4 * q;
+                    LdsVec<4>::get(p, bf[b]);
+                }
+            } else {
+                // n-contiguous B tile [k][n]: block b, lane column li is n = FN*li + b.
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float t[FN];
+                    LdsVec<FN>::get(bs + (lh * HB + 4 * q + e) * BS + wn * WTN + FN * li, t);
+#pragma unroll
+                    for (int b = 0; b < FN; ++b) bf[b][e] = t[b];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int a = 0; a < FM; ++a)
+#pragma unroll
+                    for (int b = 0; b < FN; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a][e], bf[b][e], acc[a][b],
+                                                                         0, 0, 0);
+        }
+
+        if (kt + 1 < ktiles) {
+            ca.store(a_lds + (cur ^ 1) * A_FLOATS, tid);
+            cb.store(b_lds + (cur ^ 1) * B_FLOATS, tid);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue. Accumulator element r of block (a, b) in lane (li, lh) is
+    // block row 8*(r/4) + 4*lh + r%4, block column li.
+    const float alpha = g.alpha, beta = g.beta;
+    float *const cw = g.C + (size_t)(m0 + wm * WTM) * g.ldc + (n0 + wn * WTN);
+    const int rows_left = M - (m0 + wm * WTM), cols_left = N - (n0 + wn * WTN);
+    const int ldc = g.ldc;
+#pragma unroll
+    for (int a = 0; a < FM; ++a) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ib = 8 * (r / 4) + 4 * lh + (r % 4);
+            const int row = TA ? FM * ib + a : 32 * a + ib;
+            if (row >= rows_left) continue;
+            float *crow = cw + (size_t)row * ldc;
+            if (!TB) {
+                // FN adjacent columns FN*li .. FN*li + FN-1.
+                const int col = FN * li;
+                float out[FN];
+#pragma unroll
+                for (int b = 0; b < FN; ++b) out[b] = alpha * acc[a][b][r];
+                const bool whole = g.vec_c && col + FN <= cols_left;
+                if (whole && FN == 4) {
+                    f32x4 *p = reinterpret_cast<f32x4 *>(crow + col);
+                    f32x4 v;
+                    if (beta != 0.0f) {
+                        const f32x4 c = *p;
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) v[b] = fmaf(beta, c[b], out[b]);
+                    } else {
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) v[b] = out[b];
+                    }
+                    *p = v;
+                } else if (whole && FN == 2) {
+                    f32x2 *p = reinterpret_cast<f32x2 *>(crow + col);
+                    f32x2 v;
+                    if (beta != 0.0f) {
+                        const f32x2 c = *p;
+                        v[0] = fmaf(beta, c[0], out[0]);
+                        v[1] = fmaf(beta, c[1], out[1]);
+                    } else {
+                        v[0] = out[0];
+                        v[1] = out[1];
+                    }
+                    *p = v;
+                } else {
+#pragma unroll
+                    for (int b = 0; b < FN; ++b) {
+                        if (col + b < cols_left) {
+                            float *p = crow + col + b;
+                            *p = (beta != 0.0f) ? fmaf(beta, *p, out[b]) : out[b];
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const int col = 32 * b + li;
+                    if (col < cols_left) {
+                        float *p = crow + col;
+                        const float o = alpha * acc[a][b][r];
+                        *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// C <- beta * C (beta == 0: C <- 0 without reading C), for alpha == 0 or K == 0.
+__global__ __launch_bounds__(256) void scale_c(float *C, int M, int N, int ldc, float beta) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= N) return;
+    for (int row = blockIdx.y; row < M; row += gridDim.y) {
+        float *p = C + (size_t)row * ldc + col;
+        *p = (beta == 0.0f) ? 0.0f : beta * *p;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Configuration table.
+
+using CfgL = TileCfg<128, 128, 32, 2, 2>;   // 4 waves, 64 x 64 per wave
+using CfgS = TileCfg<64, 64, 32, 2, 2>;     // 4 waves, 32 x 32 per wave
+
+struct ConfigInfo {
+    const char *name;
+    int bm, bn, nt;
+};
+
+constexpr ConfigInfo kConfigs[] = {
+    {"mfma32_128x128x32_w2x2", CfgL::BM, CfgL::BN, CfgL::NT},
+    {"mfma32_64x64x32_w2x2", CfgS::BM, CfgS::BN, CfgS::NT},
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+constexpr int kNumCus = 256;
+
+bool op_n(char t) { return t == 'N' || t == 'n'; }
+bool op_t(char t) { return t == 'T' || t == 't' || t == 'C' || t == 'c'; }
+
+int check_args(char transA, char transB, int M, int N, int K, float alpha, const float *A, int lda,
+               const float *B, int ldb, const float *C, int ldc) {
+    if (!op_n(transA) && !op_t(transA)) return MISGEMM_BAD_TRANSA;
+    if (!op_n(transB) && !op_t(transB)) return MISGEMM_BAD_TRANSB;
+    if (M < 0) return MISGEMM_BAD_M;
+    if (N < 0) return MISGEMM_BAD_N;
+    if (K < 0) return MISGEMM_BAD_K;
+    const int a_cols = op_n(transA) ? K : M;
+    const int b_cols = op_n(transB) ? N : K;
+    if (lda < (a_cols > 1 ? a_cols : 1)) return MISGEMM_BAD_LDA;
+    if (ldb < (b_cols > 1 ? b_cols : 1)) return MISGEMM_BAD_LDB;
+    if (ldc < (N > 1 ? N : 1)) return MISGEMM_BAD_LDC;
+    if (M == 0 || N == 0) return MISGEMM_SUCCESS;
+    const bool reads_ab = alpha != 0.0f && K > 0;
+    if (reads_ab && A == nullptr) return MISGEMM_NULL_A;
+    if (reads_ab && B == nullptr) return MISGEMM_NULL_B;
+    if (C == nullptr) return MISGEMM_NULL_C;
+    return MISGEMM_SUCCESS;
+}
+
+int select_config(char transA, char transB, int M, int N, int K) {
+    (void)transA;
+    (void)transB;
+    (void)K;
+    const long long tiles_l = (long long)((M + CfgL::BM - 1) / CfgL::BM) * ((N + CfgL::BN - 1) / CfgL::BN);
+    if (tiles_l >= kNumCus) return 0;
+    return 1;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <class CFG, bool TA, bool TB>
+hipError_t launch_t(const GemmArgs &g, hipStream_t stream) {
+    dim3 grid((unsigned)(g.tiles_m * g.tiles_n));
+    dim3 block(CFG::NT);
+    hipLaunchKernelGGL((sgemm_mfma32<CFG, TA, TB>), grid, block, 0, stream, g);
+    return hipGetLastError();
+}
+
+template <class CFG>
+hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream) {
+    g.tiles_m = (g.M + CFG::BM - 1) / CFG::BM;
+    g.tiles_n = (g.N + CFG::BN - 1) / CFG::BN;
+    if (!ta && !tb) return launch_t<CFG, false, false>(g, stream);
+    if (!ta && tb) return launch_t<CFG, false, true>(g, stream);
+    if (ta && !tb) return launch_t<CFG, true, false>(g, stream);
+    return launch_t<CFG, true, true>(g, stream);
+}
+
+int run(int config, char transA, char transB, int M, int N, int K, float alpha, const float *A, int lda,
+        const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+    int rc = check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc != MISGEMM_SUCCESS) return rc;
+    if (config < -1 || config >= kNumConfigs) return MISGEMM_BAD_CONFIG;
+    if (M == 0 || N == 0) return MISGEMM_SUCCESS;
+    // Tile-local offsets are 32-bit: row * ld for up to 256 rows plus a column.
+    const long long max_ld = lda > ldb ? (lda > ldc ? lda : ldc) : (ldb > ldc ? ldb : ldc);
+    if (max_ld * 256 + 256 > 0x7fffffffLL) return MISGEMM_TOO_LARGE;
+
+    if (alpha == 0.0f || K == 0) {
+        if (beta == 1.0f) return MISGEMM_SUCCESS;
+        dim3 grid((unsigned)((N + 255) / 256), (unsigned)(M < 65535 ? M : 65535));
+        hipLaunchKernelGGL(scale_c, grid, dim3(256), 0, stream, C, M, N, ldc, beta);
+        return hipGetLastError() == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
+    }
+
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldc = ldc;
+    g.alpha = alpha;
+    g.beta = beta;
+    g.vec_ab = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;
+    g.vec_c = aligned16(C) && ldc % 4 == 0;
+    const bool ta = op_t(transA), tb = op_t(transB);
+    if (config < 0) config = select_config(transA, transB, M, N, K);
+    hipError_t err;
+    switch (config) {
+        case 0: err = launch_cfg<CfgL>(ta, tb, g, stream); break;
+        default: err = launch_cfg<CfgS>(ta, tb, g, stream); break;
+    }
+    return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
+}
+
+}  // namespace
+
+extern "C" int mi_sgemm(char transA, char transB, int M, int N, int K, float alpha, const float *A, int lda,
+                        const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+    return run(-1, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+extern "C" int mi_sgemm_with_config(int config, char transA, char transB, int M, int N, int K, float alpha,
+                                    const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                                    int ldc, hipStream_t stream) {
+    if (config < 0) {
+        int rc = check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+        return rc != MISGEMM_SUCCESS ? rc : MISGEMM_BAD_CONFIG;
+    }
+    return run(config, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+extern "C" int mi_sgemm_select_config(char transA, char transB, int M, int N, int K) {
+    if (!op_n(transA) && !op_t(transA)) return MISGEMM_BAD_TRANSA;
+    if (!op_n(transB) && !op_t(transB)) return MISGEMM_BAD_TRANSB;
+    if (M < 0) return MISGEMM_BAD_M;
+    if (N < 0) return MISGEMM_BAD_N;
+    if (K < 0) return MISGEMM_BAD_K;
+    return select_config(transA, transB, M, N, K);
+}
+
+extern "C" int mi_sgemm_config_count(void) { return kNumConfigs; }
+
+extern "C" const char *mi_sgemm_config_name(int config) {
+    if (config < 0 || config >= kNumConfigs) return nullptr;
+    return kConfigs[config].name;
+}
+
+extern "C" const char *mi_sgemm_status_string(int status) {
+    switch (status) {
+        case MISGEMM_SUCCESS: return "success";
+        case MISGEMM_BAD_TRANSA: return "invalid transA (expected N, n, T, t, C or c)";
+        case MISGEMM_BAD_TRANSB: return "invalid transB (expected N, n, T, t, C or c)";
+        case MISGEMM_BAD_M: return "M < 0";
+        case MISGEMM_BAD_N: return "N < 0";
+        case MISGEMM_BAD_K: return "K < 0";
+        case MISGEMM_NULL_A: return "A is null but would be read";
+        case MISGEMM_BAD_LDA: return "lda smaller than the stored row length of A";
+        case MISGEMM_NULL_B: return "B is null but would be read";
+        case MISGEMM_BAD_LDB: return "ldb smaller than the stored row length of B";
+        case MISGEMM_NULL_C: return "C is null";
+        case MISGEMM_BAD_LDC: return "ldc < max(1, N)";
+        case MISGEMM_BAD_CONFIG: return "unknown kernel configuration id";
+        case MISGEMM_TOO_LARGE: return "leading dimension too large for 32-bit tile offsets";
+        case MISGEMM_LAUNCH_FAILED: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}

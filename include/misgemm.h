@@ -1,0 +1,115 @@
+/*
+ * misgemm -- FP32 SGEMM for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation is the BLAS SGEMM C = alpha*op(A)*op(B) + beta*C named in the
+ * overview of the itan.pw page on SGEMM optimisation for the RTX 4090, on
+ * row-major matrices as in the problem definition (问题定义) of
+ * "【CUDA】Sgemm单精度矩阵乘法" (klklkl10086.github.io), where
+ * C_ij = sum_k A_ik B_kj and a product costs 2MNK floating-point operations.
+ *
+ * Every product is computed in FP32 on the CDNA4 matrix cores
+ * (v_mfma_f32_32x32x2_f32 / v_mfma_f32_16x16x4_f32): FP32 inputs, FP32
+ * products and FP32 accumulation, with no reduced-precision emulation.
+ *
+ * Threading: every entry point is thread-safe and keeps no mutable state.
+ */
+#ifndef MISGEMM_H
+#define MISGEMM_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. Negative values name the offending argument by its position
+ * in mi_sgemm's parameter list (BLAS "info" convention). */
+#define MISGEMM_SUCCESS          0
+#define MISGEMM_BAD_TRANSA      (-1)
+#define MISGEMM_BAD_TRANSB      (-2)
+#define MISGEMM_BAD_M           (-3)
+#define MISGEMM_BAD_N           (-4)
+#define MISGEMM_BAD_K           (-5)
+#define MISGEMM_NULL_A          (-7)
+#define MISGEMM_BAD_LDA         (-8)
+#define MISGEMM_NULL_B          (-9)
+#define MISGEMM_BAD_LDB         (-10)
+#define MISGEMM_NULL_C          (-12)
+#define MISGEMM_BAD_LDC         (-13)
+#define MISGEMM_BAD_CONFIG      (-20)
+#define MISGEMM_TOO_LARGE       (-21)
+#define MISGEMM_LAUNCH_FAILED     1
+
+/*
+ * mi_sgemm: C <- alpha * op(A) * op(B) + beta * C   (FP32, row-major)
+ *
+ *   transA, transB  'N'/'n': op(X) = X;  'T'/'t'/'C'/'c': op(X) = X^T.
+ *   M, N, K         op(A) is M x K, op(B) is K x N, C is M x N; each >= 0.
+ *   A, lda          device pointer; stored A is M x K (transA 'N') or K x M
+ *                   (transA 'T'), row-major with row stride lda elements,
+ *                   lda >= max(1, number of stored columns).
+ *   B, ldb          likewise: stored B is K x N ('N') or N x K ('T').
+ *   C, ldc          device pointer; M x N row-major, ldc >= max(1, N).
+ *   alpha, beta     scalars. beta == 0: C is not read (NaN/Inf in C do not
+ *                   propagate). alpha == 0 or K == 0: A and B are not read and
+ *                   C <- beta*C. M == 0 or N == 0: nothing is done.
+ *   stream          HIP stream the work is enqueued on (0: the null stream).
+ *
+ * Semantics: C(i,j) = alpha * sum_{k<K} opA(i,k)*opB(k,j) + beta*C(i,j) for
+ * i < M, j < N, with opA(i,k) = A[i*lda+k] ('N') or A[k*lda+i] ('T') and
+ * opB(k,j) = B[k*ldb+j] ('N') or B[j*ldb+k] ('T'). Only those elements of C
+ * are written; row padding (columns N..ldc-1) is never touched. The k sum is
+ * carried in FP32 in a fixed order, so repeated calls give identical bits.
+ *
+ * Ownership: all three matrices are device memory owned by the caller. The
+ * call allocates and frees nothing, does not synchronise, and returns once
+ * the kernels are enqueued; the caller synchronises `stream` before reading
+ * C. C must not overlap A or B.
+ *
+ * Alignment: any pointer and leading dimension is accepted. 16-byte aligned
+ * pointers with lda, ldb, ldc multiples of 4 take the dwordx4 path.
+ *
+ * Errors: arguments are checked before any HIP call, in parameter order;
+ * the first bad one returns its negative code and nothing is enqueued.
+ * Sizes whose element offsets exceed 2^31-1 return MISGEMM_TOO_LARGE.
+ * MISGEMM_LAUNCH_FAILED means hipGetLastError reported an error after a
+ * launch (the error is left for the caller to inspect with hipGetLastError
+ * cleared, i.e. it has been consumed by this check).
+ */
+int mi_sgemm(char transA, char transB, int M, int N, int K,
+             float alpha, const float *A, int lda,
+             const float *B, int ldb,
+             float beta, float *C, int ldc, hipStream_t stream);
+
+/*
+ * mi_sgemm_with_config: as mi_sgemm, but with the kernel configuration chosen
+ * by the caller instead of by shape class (config ids 0 .. count-1 from
+ * mi_sgemm_config_count). Meant for tests and tuning: any config computes the
+ * same result for any valid shape. Returns MISGEMM_BAD_CONFIG for an unknown
+ * id, after the argument checks of mi_sgemm.
+ */
+int mi_sgemm_with_config(int config, char transA, char transB, int M, int N, int K,
+                         float alpha, const float *A, int lda,
+                         const float *B, int ldb,
+                         float beta, float *C, int ldc, hipStream_t stream);
+
+/*
+ * mi_sgemm_select_config: the config id mi_sgemm would use for this shape
+ * (host-side decision only; no HIP call). Returns a negative status for
+ * invalid trans letters or negative sizes.
+ */
+int mi_sgemm_select_config(char transA, char transB, int M, int N, int K);
+
+/* Number of kernel configurations, and a static name for each (NULL if the id
+ * is out of range). The string is owned by the library. */
+int mi_sgemm_config_count(void);
+const char *mi_sgemm_config_name(int config);
+
+/* Static description of a status code (never NULL; owned by the library). */
+const char *mi_sgemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MISGEMM_H */

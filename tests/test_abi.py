@@ -1,0 +1,125 @@
+"""The C-ABI library on the host: exports, argument checks, shape-class choice.
+
+Nothing here launches a kernel: every call below either fails validation or
+takes a quick return, both of which happen before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp32_gemm_nn_amd as mg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")]
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(mi_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert "mi_sgemm" in names and "mi_sgemm_status_string" in names
+    assert len(names) >= 6
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_every_declared_symbol_is_exported(name):
+    lib = ctypes.CDLL(mg.library_path)
+    assert hasattr(lib, name)
+
+
+def test_library_exports_nothing_undeclared():
+    out = os.popen(f"nm -D --defined-only {mg.library_path}").read()
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    ours = {s for s in exported if s.startswith("mi_")}
+    assert ours == set(declared_functions())
+
+
+GOOD = dict(transA="N", transB="N", M=4, N=4, K=4, alpha=1.0, A=0x1000, lda=4, B=0x2000, ldb=4,
+            beta=0.0, C=0x3000, ldc=4)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return mg.mi_sgemm(a["transA"], a["transB"], a["M"], a["N"], a["K"], a["alpha"], a["A"], a["lda"],
+                       a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(transA="X"), -1), (dict(transB="q"), -2),
+    (dict(M=-1), -3), (dict(N=-2), -4), (dict(K=-3), -5),
+    (dict(A=0), -7), (dict(lda=3), -8), (dict(transA="T", M=5, lda=4, ldc=4), -8),
+    (dict(B=0), -9), (dict(ldb=3), -10), (dict(transB="t", K=6, lda=6), -10),
+    (dict(C=0), -12), (dict(ldc=3), -13),
+    # First bad argument wins, in parameter order.
+    (dict(transA="X", M=-1, ldc=0), -1), (dict(M=-1, ldc=0), -3), (dict(lda=0, ldc=0), -8),
+])
+def test_argument_errors(kw, code):
+    assert call(**kw) == code
+    assert mg.mi_sgemm_status_string(code) not in ("", "unknown status")
+
+
+def test_quick_returns_do_not_launch():
+    # M == 0 or N == 0: success, pointers never touched (null is fine).
+    assert call(M=0, A=0, B=0, C=0) == 0
+    assert call(N=0, A=0, B=0, C=0, ldb=1, ldc=1) == 0
+    # alpha == 0 or K == 0 with beta == 1: C unchanged, nothing enqueued; A, B may be null.
+    assert call(alpha=0.0, beta=1.0, A=0, B=0) == 0
+    assert call(K=0, beta=1.0, A=0, B=0, lda=1) == 0
+
+
+def test_null_ab_allowed_when_not_read_but_c_required():
+    assert call(alpha=0.0, beta=1.0, A=0, B=0, C=0) == -12
+
+
+def test_too_large_leading_dimension():
+    assert call(lda=2**30) == mg.MisgemmError(-21).status
+    assert "too large" in mg.mi_sgemm_status_string(-21)
+
+
+def test_config_table():
+    n = mg.mi_sgemm_config_count()
+    assert n >= 2
+    names = mg.config_names()
+    assert len(set(names)) == n and all(names)
+    assert mg.mi_sgemm_config_name(n) is None and mg.mi_sgemm_config_name(-1) is None
+
+
+def test_with_config_rejects_unknown_id():
+    a = dict(GOOD)
+    args = [a[k] for k in ("transA", "transB", "M", "N", "K", "alpha", "A", "lda", "B", "ldb", "beta", "C", "ldc")]
+    n = mg.mi_sgemm_config_count()
+    assert mg.mi_sgemm_with_config(n, *args, 0) == -20
+    assert mg.mi_sgemm_with_config(-1, *args, 0) == -20
+    # Argument errors still come first.
+    args[2] = -1
+    assert mg.mi_sgemm_with_config(n, *args, 0) == -3
+
+
+def test_shape_class_selection():
+    names = mg.config_names()
+    sel = lambda *s: names[mg.mi_sgemm_select_config(*s)]
+    # 4096^2 output: 1024 tiles of 128 x 128, enough to fill 256 CUs.
+    assert "128x128" in sel("N", "N", 4096, 4096, 4096)
+    assert "128x128" in sel("T", "T", 2048, 4096, 1024)
+    # 1024^2 output: 64 such tiles only, so smaller tiles.
+    assert "128x128" not in sel("N", "N", 1024, 1024, 1024)
+    assert mg.mi_sgemm_select_config("Z", "N", 1, 1, 1) == -1
+    assert mg.mi_sgemm_select_config("N", "N", 1, 1, -1) == -5
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(mg, "_lib", None)
+    monkeypatch.setattr(mg, "library_path", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mg.mi_sgemm_config_count()

@@ -1,0 +1,275 @@
+"""HIP SGEMM vs the CPU oracle, element by element, through the C ABI.
+
+Integer-valued inputs must match bit for bit (every partial sum is an exact
+FP32 integer, so any summation order gives the same result). Uniform [-1, 1)
+inputs must satisfy max |GPU - oracle| <= 1e-3 for K <= 4096.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import fp32_gemm_nn_amd as mg
+import oracle
+from synthetic import Drand48, uniform_matrix
+from synthetic import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+OPS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
+EDGE = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def note(msg):
+    sys.__stderr__.write(f"[gpu] {msg}\n")
+    sys.__stderr__.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mg.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+class DevMat:
+    """A stored matrix in a device buffer: rows x ld, padding and guard rows
+    filled with `fill`, optionally starting `offset` floats into the buffer."""
+
+    def __init__(self, host, ld=None, fill=float("nan"), guard_rows=1, offset=0):
+        rows, cols = host.shape
+        self.rows, self.cols = rows, cols
+        self.ld = ld if ld is not None else max(cols, 1)
+        self.offset = offset
+        total = offset + (rows + guard_rows) * self.ld + 4
+        self.buf = torch.full((total,), fill, dtype=torch.float32, device="cuda")
+        if rows and cols:
+            self.view().copy_(torch.from_numpy(np.ascontiguousarray(host)).cuda())
+        self.fill = fill
+
+    def view(self):
+        return self.buf[self.offset:self.offset + self.rows * self.ld].view(self.rows, self.ld)[:, :self.cols]
+
+    @property
+    def ptr(self):
+        return self.buf.data_ptr() + 4 * self.offset
+
+    def host(self):
+        return self.view().cpu().numpy()
+
+    def outside_untouched(self):
+        """Everything except the logical rows x cols still holds `fill`."""
+        full = self.buf.cpu().numpy()
+        mask = np.ones(full.shape, bool)
+        if self.rows and self.cols:
+            idx = (self.offset + np.arange(self.rows)[:, None] * self.ld + np.arange(self.cols)[None, :]).ravel()
+            mask[idx] = False
+        rest = full[mask]
+        return np.all(np.isnan(rest)) if np.isnan(self.fill) else np.all(rest == self.fill)
+
+
+def run_gpu(case, inp, config=None, lda=None, ldb=None, ldc=None, offset=0, c_fill=-3.0, ab_fill=float("nan")):
+    lda = lda or case.lda_
+    ldb = ldb or case.ldb_
+    ldc = ldc or case.ldc_
+    A = DevMat(inp.A, lda, fill=ab_fill, offset=offset)
+    B = DevMat(inp.B, ldb, fill=ab_fill, offset=offset)
+    C = DevMat(inp.C, ldc, fill=c_fill, offset=offset)
+    args = (case.transA, case.transB, case.M, case.N, case.K, case.alpha, A.ptr, lda, B.ptr, ldb,
+            case.beta, C.ptr, ldc, torch.cuda.current_stream().cuda_stream)
+    rc = mg.mi_sgemm(*args) if config is None else mg.mi_sgemm_with_config(config, *args)
+    assert rc == 0, mg.mi_sgemm_status_string(rc)
+    torch.cuda.synchronize()
+    assert C.outside_untouched(), "C padding or guard band was written"
+    return C.host()
+
+
+def run_oracle(case, inp):
+    C = inp.C.copy()
+    rc = oracle.sgemm(case.transA, case.transB, case.M, case.N, case.K, case.alpha, inp.A, case.lda_,
+                      inp.B, case.ldb_, case.beta, C, case.ldc_)
+    assert rc == 0
+    return C
+
+
+def compare(case, got, want, exact):
+    if exact:
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{case.name}: {len(bad)} mismatches, first at {bad[0]}: {got[tuple(bad[0])]} vs {want[tuple(bad[0])]}"
+        return
+    assert np.all(np.isfinite(got))
+    d = got.astype(np.float64) - want.astype(np.float64)
+    maxabs = float(np.abs(d).max()) if d.size else 0.0
+    note(f"{case.name}: max|err| {maxabs:.3e}  mean err {float(d.mean()) if d.size else 0:.2e}")
+    assert maxabs <= TOL, f"{case.name}: max abs error {maxabs}"
+
+
+def is_exact(case):
+    return case.fill != "uniform"
+
+
+# --- the workload configurations -----------------------------------------------------
+
+CONFIG_CASES = [W.C1, W.C2, W.C2_INT, W.C4, *W.C5A, W.C5B]
+
+
+@pytest.mark.parametrize("case", CONFIG_CASES, ids=lambda c: c.name)
+def test_workload_configs(case):
+    note(f"config {case.name} {case.transA}{case.transB} {case.M}x{case.N}x{case.K}")
+    inp = W.make_inputs(case)
+    compare(case, run_gpu(case, inp), run_oracle(case, inp), is_exact(case))
+
+
+@pytest.mark.parametrize("n", W.C3_SIZES)
+def test_square_sweep(n):
+    case = W.c3(n)
+    note(f"sweep {case.name}")
+    inp = W.make_inputs(case)
+    compare(case, run_gpu(case, inp), run_oracle(case, inp), False)
+
+
+INT_CASES = [
+    W.C1.with_(name="int_c1", fill="int_trunc"),
+    W.C2.with_(name="int_floor_1024", fill="int_floor"),
+    W.C4.with_(name="int_4096", fill="int_trunc"),
+    W.C5B.with_(name="int_skinny", fill="int_rand"),
+    *[c.with_(name="int_" + c.name, fill="int_rand", alpha=2.0, beta=-1.0) for c in W.C5A],
+    *[W.c3(n).with_(name=f"int_sweep_{n}", fill="int_rand", alpha=0.5, beta=-2.0) for n in (256, 768, 1280, 2304)],
+]
+
+
+@pytest.mark.parametrize("case", INT_CASES, ids=lambda c: c.name)
+def test_integer_inputs_bit_exact(case):
+    note(f"int {case.name}")
+    inp = W.make_inputs(case)
+    compare(case, run_gpu(case, inp), run_oracle(case, inp), True)
+
+
+# --- every kernel configuration on ragged shapes ------------------------------------------
+
+def _edge_triples(count, seed):
+    rng = np.random.default_rng(seed)
+    trip = [(e, e, e) for e in EDGE]
+    trip += [tuple(int(v) for v in rng.choice(EDGE, 3)) for _ in range(count)]
+    return trip
+
+
+@pytest.mark.parametrize("ta,tb", OPS)
+@pytest.mark.parametrize("config", range(2))
+def test_edge_shapes_every_config(ta, tb, config):
+    assert config < mg.mi_sgemm_config_count()
+    scal = [(1.0, 0.0), (-1.0, 1.0), (2.0, -1.0), (0.5, 0.5), (1.0, 1.0)]
+    for t, (M, N, K) in enumerate(_edge_triples(30, 100 + config)):
+        alpha, beta = scal[t % len(scal)]
+        case = W.Case(f"edge_{ta}{tb}_{M}x{N}x{K}_cfg{config}", ta, tb, M, N, K, alpha, beta,
+                      seed=1000 + t, fill="int_rand")
+        note(case.name)
+        inp = W.make_inputs(case)
+        if beta == 0.0:
+            inp.C[:] = np.nan                       # beta == 0: C must not be read
+        compare(case, run_gpu(case, inp, config=config), run_oracle(case, inp), True)
+
+
+@pytest.mark.parametrize("config", range(2))
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_every_config_uniform_medium(config, ta, tb):
+    case = W.Case(f"medium_{ta}{tb}_cfg{config}", ta, tb, 333, 517, 429, 1.5, 0.5, seed=77)
+    note(case.name)
+    inp = W.make_inputs(case)
+    compare(case, run_gpu(case, inp, config=config), run_oracle(case, inp), False)
+
+
+# --- layouts: leading-dimension padding, alignment, poisoned padding ------------------------
+
+@pytest.mark.parametrize("ta,tb", OPS)
+@pytest.mark.parametrize("pad,offset", [(0, 1), (3, 0), (4, 0), (5, 3), (64, 2)])
+def test_padding_and_alignment(ta, tb, pad, offset):
+    case = W.Case(f"ld_{ta}{tb}_p{pad}_o{offset}", ta, tb, 200, 150, 131, 1.0, 1.0, seed=9, fill="int_rand")
+    note(case.name)
+    inp = W.make_inputs(case)
+    got = run_gpu(case, inp, lda=case.lda_ + pad, ldb=case.ldb_ + pad, ldc=case.ldc_ + pad, offset=offset)
+    compare(case, got, run_oracle(case, inp), True)
+
+
+def test_large_tile_path_with_padding():
+    case = W.Case("ld_large", "N", "N", 2048, 2048, 256, 1.0, 0.0, seed=10, fill="int_rand")
+    inp = W.make_inputs(case)
+    got = run_gpu(case, inp, lda=260, ldb=2052, ldc=2056)
+    compare(case, got, run_oracle(case, inp), True)
+
+
+# --- BLAS semantics of the scalars and empty sizes ------------------------------------------
+
+def test_beta_zero_ignores_nan_c():
+    case = W.Case("beta0_nan", "N", "N", 300, 260, 70, 1.0, 0.0, seed=12)
+    inp = W.make_inputs(case)
+    inp.C[:] = np.nan
+    got = run_gpu(case, inp)
+    inp.C[:] = 0.0
+    compare(case, got, run_oracle(case, inp), False)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, -2.0])
+def test_alpha_zero_scales_c_without_reading_ab(beta):
+    case = W.Case("alpha0", "N", "T", 130, 70, 50, 0.0, beta, seed=13)
+    inp = W.make_inputs(case)
+    inp.C[:] = uniform_matrix(Drand48(14), 130, 70)
+    inp.A[:] = np.nan
+    inp.B[:] = np.nan
+    got = run_gpu(case, inp)
+    want = run_oracle(case, inp)
+    assert np.array_equal(got, want)
+
+
+def test_k_zero_scales_c():
+    case = W.Case("k0", "N", "N", 100, 90, 0, 1.0, -0.5, seed=15)
+    inp = W.make_inputs(case)
+    inp.C[:] = uniform_matrix(Drand48(16), 100, 90)
+    got = run_gpu(case, inp)
+    assert np.array_equal(got, run_oracle(case, inp))
+
+
+def test_alpha_zero_beta_one_leaves_c():
+    case = W.Case("noop", "N", "N", 64, 64, 64, 0.0, 1.0, seed=17)
+    inp = W.make_inputs(case)
+    inp.C[:] = np.nan
+    got = run_gpu(case, inp)
+    assert np.all(np.isnan(got))
+
+
+@pytest.mark.parametrize("M,N", [(0, 5), (5, 0), (0, 0)])
+def test_empty_output(M, N):
+    C = torch.full((16,), 7.0, device="cuda")
+    rc = mg.mi_sgemm("N", "N", M, N, 3, 1.0, 0, 3, 0, max(N, 1), 0.0, C.data_ptr(), max(N, 1),
+                     torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0 and bool(torch.all(C == 7.0))
+
+
+# --- determinism ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", [W.C4, W.C5A[3], W.C5B, W.C1], ids=lambda c: c.name)
+def test_run_to_run_bitwise(case):
+    inp = W.make_inputs(case)
+    a = run_gpu(case, inp)
+    b = run_gpu(case, inp)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# --- the torch-tensor wrapper ---------------------------------------------------------------
+
+def test_tensor_wrapper_matches_oracle():
+    case = W.Case("wrapper", "T", "N", 257, 129, 65, 1.5, 0.5, seed=18)
+    inp = W.make_inputs(case)
+    A = torch.from_numpy(inp.A).cuda()
+    B = torch.from_numpy(inp.B).cuda()
+    C = torch.from_numpy(inp.C.copy()).cuda()
+    mg.sgemm("T", "N", 1.5, A, B, 0.5, C)
+    torch.cuda.synchronize()
+    compare(case, C.cpu().numpy(), run_oracle(case, inp), False)
+    with pytest.raises(ValueError):
+        mg.sgemm("N", "N", 1.0, A, B, 0.0, C)         # shapes do not chain
