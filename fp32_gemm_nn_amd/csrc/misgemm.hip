@@ -152,6 +152,37 @@ struct TileCopy {
     }
 };
 
+template <int n> struct VecOf;
+template <> struct VecOf<2> { using type = f32x2; };
+template <> struct VecOf<4> { using type = f32x4; };
+
+// C <- out + beta*C over n adjacent elements of one row, as one vector access
+// when `whole` (all n in range and aligned), else element by element for the
+// first `valid` of them. beta == 0: C is not read.
+template <int n>
+__device__ __forceinline__ void store_run(float *p, const float (&out)[n], float beta, bool whole, int valid) {
+    if constexpr (n == 2 || n == 4) {
+        if (whole) {
+            using V = typename VecOf<n>::type;
+            V *vp = reinterpret_cast<V *>(p);
+            V v;
+            if (beta != 0.0f) {
+                const V c = *vp;
+#pragma unroll
+                for (int b = 0; b < n; ++b) v[b] = fmaf(beta, c[b], out[b]);
+            } else {
+#pragma unroll
+                for (int b = 0; b < n; ++b) v[b] = out[b];
+            }
+            *vp = v;
+            return;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < n; ++b)
+        if (b < valid) p[b] = (beta != 0.0f) ? fmaf(beta, p[b], out[b]) : out[b];
+}
+
 // Launch index -> (tile row, tile column). Workgroup b runs on XCD b % 8; the
 // j-th workgroup of XCD x is given logical tile prefix(x) + j, so each XCD
 // walks one contiguous run of logical tiles. Logical tiles are ordered in
@@ -315,40 +346,7 @@ __global__ __launch_bounds__(CFG::NT) void sgemm_mfma32(GemmArgs g) {
                 float out[FN];
 #pragma unroll
                 for (int b = 0; b < FN; ++b) out[b] = alpha * acc[a][b][r];
-                const bool whole = g.vec_c && col + FN <= cols_left;
-                if (whole && FN == 4) {
-                    f32x4 *p = reinterpret_cast<f32x4 *>(crow + col);
-                    f32x4 v;
-                    if (beta != 0.0f) {
-                        const f32x4 c = *p;
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) v[b] = fmaf(beta, c[b], out[b]);
-                    } else {
-#pragma unroll
-                        for (int b = 0; b < 4; ++b) v[b] = out[b];
-                    }
-                    *p = v;
-                } else if (whole && FN == 2) {
-                    f32x2 *p = reinterpret_cast<f32x2 *>(crow + col);
-                    f32x2 v;
-                    if (beta != 0.0f) {
-                        const f32x2 c = *p;
-                        v[0] = fmaf(beta, c[0], out[0]);
-                        v[1] = fmaf(beta, c[1], out[1]);
-                    } else {
-                        v[0] = out[0];
-                        v[1] = out[1];
-                    }
-                    *p = v;
-                } else {
-#pragma unroll
-                    for (int b = 0; b < FN; ++b) {
-                        if (col + b < cols_left) {
-                            float *p = crow + col + b;
-                            *p = (beta != 0.0f) ? fmaf(beta, *p, out[b]) : out[b];
-                        }
-                    }
-                }
+                store_run<FN>(crow + col, out, beta, g.vec_c && col + FN <= cols_left, cols_left - col);
             } else {
 #pragma unroll
                 for (int b = 0; b < FN; ++b) {
@@ -360,6 +358,151 @@ __global__ __launch_bounds__(CFG::NT) void sgemm_mfma32(GemmArgs g) {
                     }
                 }
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny kernel: few rows of C (M <= 32 is its intended class), where the cost
+// is one pass over op(B) from HBM (4KN bytes against 2MKN flops: under 20
+// flop/byte for M <= 32, below the MI355X ridge of 157.3 TFLOP/s / 8 TB/s).
+//
+// One workgroup owns 16 columns of C and 16*MB rows (MB = 1 or 2), over all
+// of K. Its kSkinnyWaves waves split K into contiguous runs of 16-row chunks
+// and each keeps a 16 x 16 FP32 accumulator block per row block, fed by
+// v_mfma_f32_16x16x4_f32. Lane (c, q) = (lane % 16, lane / 16) supplies
+// column c of op(B) and row c of op(A) for k slot q; within a chunk, MFMA j
+// takes k = k0 + 4q + j (a k-permutation shared by both operands), so the
+// lane's four A values are one 16-byte load and, for B stored k-contiguous
+// ('T'), so are its four B values. B ('N') is read one element per lane in
+// exactly the MFMA layout: each load instruction covers 4 rows x 64 bytes.
+// kSkinnyUnroll chunks of loads are in flight per wave before their MFMAs.
+// The waves' partial blocks are summed through LDS in wave order (a fixed
+// order: repeated calls give identical bits), then alpha/beta are applied
+// and the block is stored with masks for M and N.
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyUnroll = 8;
+
+// Loads of one group of U chunks (k rows kc*16 .. (kc+U)*16) for one lane,
+// zero where out of range.
+template <int U, int MB, bool TA, bool TB>
+struct SkinnyFrag {
+    float b[U][4];
+    float a[U][MB][4];
+
+    __device__ __forceinline__ void load(const GemmArgs &g, const float *bcol, bool col_ok, int m0, int c,
+                                         int q, int kc, int kc1, bool vec) {
+        const int M = g.M, K = g.K, lda = g.lda, ldb = g.ldb;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool chunk_ok = kc + u < kc1;
+            const int kq = (kc + u) * 16 + 4 * q;            // this lane's first k in the chunk
+            const bool full = chunk_ok && kq + 4 <= K;
+            if (TB && vec && full && col_ok) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(bcol + kq);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[u][j] = v[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int k = kq + j;
+                    const bool ok = chunk_ok && col_ok && k < K;
+                    b[u][j] = ok ? (TB ? bcol[k] : bcol[(size_t)k * ldb]) : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = m0 + 16 * mb + c;
+                const bool row_ok = row < M;
+                if (!TA && vec && full && row_ok) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a[u][mb][j] = v[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int k = kq + j;
+                        const bool ok = chunk_ok && row_ok && k < K;
+                        a[u][mb][j] = ok ? (TA ? g.A[(size_t)k * lda + row] : g.A[(size_t)row * lda + k]) : 0.0f;
+                    }
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void mma(f32x4 (&acc)[MB]) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][mb][j], b[u][j], acc[mb], 0, 0, 0);
+    }
+};
+
+template <int MB, bool TA, bool TB>
+__global__ __launch_bounds__(64 * kSkinnyWaves) void sgemm_skinny16(GemmArgs g) {
+    constexpr int NT = 64 * kSkinnyWaves, U = kSkinnyUnroll;
+    __shared__ float red[kSkinnyWaves][MB][256];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c = lane & 15, q = lane >> 4;
+    // Column slabs: the j-th workgroup on XCD x takes slab prefix(x) + j, so
+    // each XCD reads one contiguous band of columns and its L2 lines are
+    // shared by neighbouring slabs.
+    const int total = gridDim.x, bid = blockIdx.x;
+    const int xq = total / kXcds, xr = total % kXcds, x = bid % kXcds;
+    const int slab = x * xq + (x < xr ? x : xr) + bid / kXcds;
+    const int n0 = slab * 16, m0 = blockIdx.y * 16 * MB;
+    const int M = g.M, N = g.N, K = g.K;
+    const bool vec = g.vec_ab != 0;
+
+    const int nchunks = (K + 15) / 16;
+    const int per = (nchunks + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int kc0 = w * per;
+    const int kc1 = min(nchunks, kc0 + per);
+    const bool col_ok = n0 + c < N;
+    // op(B)(k, n0 + c): B[k*ldb + n0 + c] ('N') or B[(n0 + c)*ldb + k] ('T').
+    const float *bcol = TB ? g.B + (size_t)(col_ok ? n0 + c : 0) * g.ldb : g.B + (col_ok ? n0 + c : 0);
+
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Two register buffers: the loads of the next U chunks are in flight while
+    // the MFMAs of the current ones run.
+    SkinnyFrag<U, MB, TA, TB> f0, f1;
+    f0.load(g, bcol, col_ok, m0, c, q, kc0, kc1, vec);
+    for (int kc = kc0; kc < kc1; kc += 2 * U) {
+        f1.load(g, bcol, col_ok, m0, c, q, kc + U, kc1, vec);
+        f0.mma(acc);
+        if (kc + 2 * U >= kc1) {
+            f1.mma(acc);
+            break;
+        }
+        f0.load(g, bcol, col_ok, m0, c, q, kc + 2 * U, kc1, vec);
+        f1.mma(acc);
+    }
+
+    // Accumulator element r of lane (c, q) is block row 4q + r, column c.
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[w][mb][(4 * q + r) * 16 + c] = acc[mb][r];
+    __syncthreads();
+
+    const float alpha = g.alpha, beta = g.beta;
+    for (int t = tid; t < MB * 256; t += NT) {
+        const int mb = t >> 8, rc = t & 255;
+        const int row = m0 + 16 * mb + (rc >> 4), col = n0 + (rc & 15);
+        float s = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kSkinnyWaves; ++v) s += red[v][mb][rc];
+        if (row < M && col < N) {
+            float *p = g.C + (size_t)row * g.ldc + col;
+            const float o = alpha * s;
+            *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
         }
     }
 }
@@ -388,7 +531,10 @@ struct ConfigInfo {
 constexpr ConfigInfo kConfigs[] = {
     {"mfma32_128x128x32_w2x2", CfgL::BM, CfgL::BN, CfgL::NT},
     {"mfma32_64x64x32_w2x2", CfgS::BM, CfgS::BN, CfgS::NT},
+    {"skinny_mfma16_16cols_splitk8", 32, 16, 64 * kSkinnyWaves},
 };
+constexpr int kSkinnyConfig = 2;
+constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kNumCus = 256;
 
@@ -419,6 +565,7 @@ int select_config(char transA, char transB, int M, int N, int K) {
     (void)transA;
     (void)transB;
     (void)K;
+    if (M <= kSkinnyMaxM) return kSkinnyConfig;
     const long long tiles_l = (long long)((M + CfgL::BM - 1) / CfgL::BM) * ((N + CfgL::BN - 1) / CfgL::BN);
     if (tiles_l >= kNumCus) return 0;
     return 1;
@@ -432,6 +579,26 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t stream) {
     dim3 block(CFG::NT);
     hipLaunchKernelGGL((sgemm_mfma32<CFG, TA, TB>), grid, block, 0, stream, g);
     return hipGetLastError();
+}
+
+template <int MB, bool TA, bool TB>
+hipError_t launch_skinny_t(const GemmArgs &g, hipStream_t stream) {
+    dim3 grid((unsigned)((g.N + 15) / 16), (unsigned)((g.M + 16 * MB - 1) / (16 * MB)));
+    hipLaunchKernelGGL((sgemm_skinny16<MB, TA, TB>), grid, dim3(64 * kSkinnyWaves), 0, stream, g);
+    return hipGetLastError();
+}
+
+template <int MB>
+hipError_t launch_skinny_mb(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) {
+    if (!ta && !tb) return launch_skinny_t<MB, false, false>(g, stream);
+    if (!ta && tb) return launch_skinny_t<MB, false, true>(g, stream);
+    if (ta && !tb) return launch_skinny_t<MB, true, false>(g, stream);
+    return launch_skinny_t<MB, true, true>(g, stream);
+}
+
+hipError_t launch_skinny(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) {
+    if (g.M <= 16) return launch_skinny_mb<1>(ta, tb, g, stream);
+    return launch_skinny_mb<2>(ta, tb, g, stream);
 }
 
 template <class CFG>
@@ -453,6 +620,9 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     // Tile-local offsets are 32-bit: row * ld for up to 256 rows plus a column.
     const long long max_ld = lda > ldb ? (lda > ldc ? lda : ldc) : (ldb > ldc ? ldb : ldc);
     if (max_ld * 256 + 256 > 0x7fffffffLL) return MISGEMM_TOO_LARGE;
+    // Grid limits: one workgroup per output tile (x), and row blocks of the
+    // skinny kernel (y, at most 65535).
+    if ((long long)((N + 15) / 16) * ((M + 15) / 16) > 0x7fffffffLL) return MISGEMM_TOO_LARGE;
 
     if (alpha == 0.0f || K == 0) {
         if (beta == 1.0f) return MISGEMM_SUCCESS;
@@ -477,10 +647,12 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     g.vec_c = aligned16(C) && ldc % 4 == 0;
     const bool ta = op_t(transA), tb = op_t(transB);
     if (config < 0) config = select_config(transA, transB, M, N, K);
+    if (config == kSkinnyConfig && (M + 2 * 16 - 1) / (2 * 16) > 65535) return MISGEMM_TOO_LARGE;
     hipError_t err;
     switch (config) {
         case 0: err = launch_cfg<CfgL>(ta, tb, g, stream); break;
-        default: err = launch_cfg<CfgS>(ta, tb, g, stream); break;
+        case 1: err = launch_cfg<CfgS>(ta, tb, g, stream); break;
+        default: err = launch_skinny(ta, tb, g, stream); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }
@@ -533,7 +705,7 @@ extern "C" const char *mi_sgemm_status_string(int status) {
         case MISGEMM_NULL_C: return "C is null";
         case MISGEMM_BAD_LDC: return "ldc < max(1, N)";
         case MISGEMM_BAD_CONFIG: return "unknown kernel configuration id";
-        case MISGEMM_TOO_LARGE: return "leading dimension too large for 32-bit tile offsets";
+        case MISGEMM_TOO_LARGE: return "problem too large (leading dimension beyond 32-bit tile offsets, or grid too large)";
         case MISGEMM_LAUNCH_FAILED: return "HIP kernel launch failed";
         default: return "unknown status";
     }

@@ -114,6 +114,10 @@ def test_shape_class_selection():
     assert "128x128" in sel("T", "T", 2048, 4096, 1024)
     # 1024^2 output: 64 such tiles only, so smaller tiles.
     assert "128x128" not in sel("N", "N", 1024, 1024, 1024)
+    # M <= 32: the skinny, bandwidth-bound kernel.
+    assert "skinny" in sel("N", "N", 16, 4096, 4096)
+    assert "skinny" in sel("T", "T", 32, 100, 7)
+    assert "skinny" not in sel("N", "N", 33, 4096, 4096)
     assert mg.mi_sgemm_select_config("Z", "N", 1, 1, 1) == -1
     assert mg.mi_sgemm_select_config("N", "N", 1, 1, -1) == -5
 

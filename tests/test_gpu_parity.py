@@ -149,6 +149,18 @@ def test_integer_inputs_bit_exact(case):
     compare(case, run_gpu(case, inp), run_oracle(case, inp), True)
 
 
+@pytest.mark.parametrize("ta,tb", OPS)
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 31, 32])
+def test_skinny_rows_every_op(ta, tb, M):
+    case = W.Case(f"skinny_{ta}{tb}_M{M}", ta, tb, M, 1000, 1037, 2.0, -1.0, seed=40 + M, fill="int_rand")
+    note(case.name)
+    inp = W.make_inputs(case)
+    compare(case, run_gpu(case, inp), run_oracle(case, inp), True)
+    ucase = case.with_(name=case.name + "_uniform", fill="uniform", alpha=1.0, beta=1.0, K=4096)
+    inp = W.make_inputs(ucase)
+    compare(ucase, run_gpu(ucase, inp), run_oracle(ucase, inp), False)
+
+
 # --- every kernel configuration on ragged shapes ------------------------------------------
 
 def _edge_triples(count, seed):
@@ -158,10 +170,12 @@ def _edge_triples(count, seed):
     return trip
 
 
+NCONFIG = mg.mi_sgemm_config_count()
+
+
 @pytest.mark.parametrize("ta,tb", OPS)
-@pytest.mark.parametrize("config", range(2))
+@pytest.mark.parametrize("config", range(NCONFIG))
 def test_edge_shapes_every_config(ta, tb, config):
-    assert config < mg.mi_sgemm_config_count()
     scal = [(1.0, 0.0), (-1.0, 1.0), (2.0, -1.0), (0.5, 0.5), (1.0, 1.0)]
     for t, (M, N, K) in enumerate(_edge_triples(30, 100 + config)):
         alpha, beta = scal[t % len(scal)]
@@ -174,7 +188,7 @@ def test_edge_shapes_every_config(ta, tb, config):
         compare(case, run_gpu(case, inp, config=config), run_oracle(case, inp), True)
 
 
-@pytest.mark.parametrize("config", range(2))
+@pytest.mark.parametrize("config", range(NCONFIG))
 @pytest.mark.parametrize("ta,tb", OPS)
 def test_every_config_uniform_medium(config, ta, tb):
     case = W.Case(f"medium_{ta}{tb}_cfg{config}", ta, tb, 333, 517, 429, 1.5, 0.5, seed=77)
