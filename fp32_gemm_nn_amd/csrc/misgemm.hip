@@ -45,6 +45,10 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "misgemm.h"
 
 namespace {
@@ -507,6 +511,249 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void sgemm_skinny16(GemmArgs g) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny kernel with K split over workgroups. A 16-column slab per workgroup
+// (above) reads B in 64-byte pieces, which HBM serves at well under its
+// streaming rate; here a workgroup owns a band of kBandCols = 128 columns
+// (512-byte rows) and 1/S of K, so S workgroups share a band and the grid
+// still fills the chip.
+//
+// Lane (c, q) = (lane % 16, lane / 16). Within a 16-row chunk, MFMA step j
+// takes k = k0 + 4q + j for both operands (a k-permutation). For B stored
+// n-contiguous ('N') the lane loads four columns n0 + 64h + 4c .. +3 of row
+// k as one 16-byte load (h = 0, 1 picks the half band), and MFMA block
+// (h, e) takes column n0 + 64h + 4c + e: one load instruction covers
+// 4 rows x 256 bytes and feeds four 16x16x4 MFMAs. For B stored k-contiguous
+// ('T'), block b takes columns n0 + 16b + c and the lane's four k values
+// are one 16-byte load.
+//
+// Reduction, in a fixed order at every level: the waves of a
+// workgroup split its k range and are summed through LDS in wave order; with
+// S > 1 each workgroup then writes its partial block to the workspace and
+// increments the band's counter; the one that brings the counter to S sums
+// the S partials in split order, applies alpha/beta, stores C and resets the
+// counter for the next call. No workgroup waits on another, so no grid-wide
+// residency is assumed.
+constexpr int kBandCols = 128;
+constexpr int kBandWaves = 8;
+constexpr int kMaxSplits = 32;
+// Waves per workgroup: eight for one row block; four for two, so that each
+// wave may use 512 registers (the two-row-block fragments need ~260).
+template <int MB> constexpr int band_waves() { return MB == 1 ? kBandWaves : kBandWaves / 2; }
+// 16-row chunks per register buffer.
+template <int MB> constexpr int band_chunks() { return 2; }
+
+struct SplitArgs {
+    GemmArgs g;
+    float *ws;            // [tile][split][16*MB*kBandCols] partial blocks
+    int *counters;        // one per tile; zero between calls
+    int splits;           // S
+    int rows_per_split;   // multiple of 16
+};
+
+template <int MB, bool TA, bool TB>
+struct BandFrag {
+    static constexpr int kBandChunks = band_chunks<MB>();
+    f32x4 b[kBandChunks][8];
+    float a[kBandChunks][MB][4];
+
+    // Chunk u covers k0 = kc + 16u .. +15, valid below kend.
+    __device__ __forceinline__ void load(const GemmArgs &g, int m0, int n0, int c, int q, int kc, int kend,
+                                         bool vec) {
+        const int M = g.M, N = g.N, lda = g.lda, ldb = g.ldb;
+#pragma unroll
+        for (int u = 0; u < kBandChunks; ++u) {
+            const int kq = kc + 16 * u + 4 * q;
+            if (!TB) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int col = n0 + 64 * h + 4 * c;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int k = kq + j;
+                        const float *p = g.B + (size_t)k * ldb + col;
+                        if (vec && k < kend && col + 3 < N) {
+                            b[u][4 * h + j] = *reinterpret_cast<const f32x4 *>(p);
+                        } else {
+                            f32x4 t;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) t[e] = (k < kend && col + e < N) ? p[e] : 0.0f;
+                            b[u][4 * h + j] = t;
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int blk = 0; blk < 8; ++blk) {
+                    const int n = n0 + 16 * blk + c;
+                    const float *p = g.B + (size_t)n * ldb + kq;
+                    if (vec && n < N && kq + 3 < kend) {
+                        b[u][blk] = *reinterpret_cast<const f32x4 *>(p);
+                    } else {
+                        f32x4 t;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) t[e] = (n < N && kq + e < kend) ? p[e] : 0.0f;
+                        b[u][blk] = t;
+                    }
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = m0 + 16 * mb + c;
+                if (!TA && vec && row < M && kq + 3 < kend) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a[u][mb][j] = v[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int k = kq + j;
+                        const bool ok = row < M && k < kend;
+                        a[u][mb][j] = ok ? (TA ? g.A[(size_t)k * lda + row] : g.A[(size_t)row * lda + k]) : 0.0f;
+                    }
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void mma(f32x4 (&acc)[MB][8]) const {
+#pragma unroll
+        for (int u = 0; u < kBandChunks; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int blk = 0; blk < 8; ++blk) {
+                        // 'N': block blk = 4h + e takes element e of the row-j load of half h.
+                        const float bv = TB ? b[u][blk][j] : b[u][4 * (blk / 4) + j][blk % 4];
+                        acc[mb][blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u][mb][j], bv, acc[mb][blk], 0, 0, 0);
+                    }
+    }
+};
+
+template <int MB, bool TA, bool TB>
+__global__ __launch_bounds__(64 * band_waves<MB>()) void sgemm_skinny_band(SplitArgs sa) {
+    constexpr int W = band_waves<MB>();
+    constexpr int NT = 64 * W;
+    constexpr int T = 16 * MB * kBandCols;       // outputs per workgroup
+    __shared__ float red[W][T];
+    __shared__ int is_last;
+
+    const GemmArgs &g = sa.g;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c = lane & 15, q = lane >> 4;
+    const int S = sa.splits;
+    // Launch index -> (band, split): each XCD takes a contiguous run, so the
+    // S workgroups of a band share an L2 whenever the run allows.
+    const int total = gridDim.x, bid = blockIdx.x;
+    const int xq = total / kXcds, xr = total % kXcds, x = bid % kXcds;
+    const int logical = x * xq + (x < xr ? x : xr) + bid / kXcds;
+    const int band = logical / S, split = logical % S;
+    const int n0 = band * kBandCols, m0 = blockIdx.y * 16 * MB;
+    const int tile = blockIdx.y * (total / S) + band;
+    const int M = g.M, N = g.N, K = g.K;
+    const bool vec = g.vec_ab != 0;
+
+    const int ks = split * sa.rows_per_split;
+    const int ke = min(K, ks + sa.rows_per_split);
+    const int rpw = ((sa.rows_per_split / 16 + W - 1) / W) * 16;
+    const int kw0 = ks + w * rpw;
+    const int kw1 = min(ke, kw0 + rpw);
+
+    f32x4 acc[MB][8];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) acc[mb][blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    constexpr int STEP = 16 * band_chunks<MB>();
+    if (kw0 < kw1) {
+        BandFrag<MB, TA, TB> f0, f1;
+        f0.load(g, m0, n0, c, q, kw0, kw1, vec);
+        for (int kc = kw0; kc < kw1; kc += 2 * STEP) {
+            if (kc + STEP < kw1) f1.load(g, m0, n0, c, q, kc + STEP, kw1, vec);
+            f0.mma(acc);
+            if (kc + STEP >= kw1) break;
+            if (kc + 2 * STEP < kw1) f0.load(g, m0, n0, c, q, kc + 2 * STEP, kw1, vec);
+            f1.mma(acc);
+        }
+    }
+
+    // Canonical block layout: index = row * kBandCols + col.
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            const int col = TB ? 16 * blk + c : 64 * (blk / 4) + 4 * c + (blk % 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[w][(16 * mb + 4 * q + r) * kBandCols + col] = acc[mb][blk][r];
+        }
+    __syncthreads();
+
+    const float alpha = g.alpha, beta = g.beta;
+    auto finish = [&](int idx, float sum) {
+        const int row = m0 + idx / kBandCols, col = n0 + idx % kBandCols;
+        if (row < M && col < N) {
+            float *p = g.C + (size_t)row * g.ldc + col;
+            const float o = alpha * sum;
+            *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
+        }
+    };
+
+    if (S == 1) {
+        for (int idx = tid; idx < T; idx += NT) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int v = 0; v < W; ++v) sum += red[v][idx];
+            finish(idx, sum);
+        }
+        return;
+    }
+
+    // Partials are written and read with system-scope relaxed atomics, i.e.
+    // stores written through to, and loads served from, the point where all
+    // XCDs are coherent; each thread's stores have completed (s_waitcnt 0)
+    // before the barrier that precedes the counter increment, and the last
+    // workgroup only loads after it has seen the count. This avoids the
+    // whole-L2 write-back and invalidate a device-scope fence costs here.
+    float *part = sa.ws + ((size_t)tile * S + split) * T;
+    for (int idx = tid; idx < T; idx += NT) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < W; ++v) sum += red[v][idx];
+        __hip_atomic_store(part + idx, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+        is_last = __hip_atomic_fetch_add(&sa.counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == S - 1;
+    __syncthreads();
+    if (!is_last) return;
+    // All S loads of an output are issued before any is summed (the sum
+    // itself still runs in split order).
+    const float *parts = sa.ws + (size_t)tile * S * T;
+    for (int idx = tid; idx < T; idx += NT) {
+        float v[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            v[sp] = sp < S ? __hip_atomic_load(parts + (size_t)sp * T + idx, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_SYSTEM)
+                           : 0.0f;
+        float sum = 0.0f;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < S) sum += v[sp];
+        finish(idx, sum);
+    }
+    if (tid == 0) __hip_atomic_store(&sa.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__global__ __launch_bounds__(256) void zero_ints(int *p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
 // C <- beta * C (beta == 0: C <- 0 without reading C), for alpha == 0 or K == 0.
 __global__ __launch_bounds__(256) void scale_c(float *C, int M, int N, int ldc, float beta) {
     const int col = blockIdx.x * 256 + threadIdx.x;
@@ -532,8 +779,10 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_128x128x32_w2x2", CfgL::BM, CfgL::BN, CfgL::NT},
     {"mfma32_64x64x32_w2x2", CfgS::BM, CfgS::BN, CfgS::NT},
     {"skinny_mfma16_16cols_splitk8", 32, 16, 64 * kSkinnyWaves},
+    {"skinny_mfma16_band128_splitk", 32, kBandCols, 64 * kBandWaves},
 };
 constexpr int kSkinnyConfig = 2;
+constexpr int kBandConfig = 3;
 constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kNumCus = 256;
@@ -565,7 +814,7 @@ int select_config(char transA, char transB, int M, int N, int K) {
     (void)transA;
     (void)transB;
     (void)K;
-    if (M <= kSkinnyMaxM) return kSkinnyConfig;
+    if (M <= kSkinnyMaxM) return kBandConfig;
     const long long tiles_l = (long long)((M + CfgL::BM - 1) / CfgL::BM) * ((N + CfgL::BN - 1) / CfgL::BN);
     if (tiles_l >= kNumCus) return 0;
     return 1;
@@ -579,6 +828,105 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t stream) {
     dim3 block(CFG::NT);
     hipLaunchKernelGGL((sgemm_mfma32<CFG, TA, TB>), grid, block, 0, stream, g);
     return hipGetLastError();
+}
+
+// Workspace for the split-K reduction, one per (device, stream) so that calls
+// on different streams never share partials or counters. Allocated on the
+// first call that needs it and kept until the process ends.
+constexpr size_t kWsFloats = size_t(4) << 20;   // 16 MiB of partial blocks
+constexpr int kWsCounters = 1 << 16;
+
+struct Workspace {
+    float *partials = nullptr;
+    int *counters = nullptr;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+// Returns nullptr if no workspace can be had (the caller then runs unsplit).
+const Workspace *get_workspace(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto key = std::make_pair(dev, stream);
+    auto it = g_ws.find(key);
+    if (it != g_ws.end()) return &it->second;
+    Workspace w;
+    if (hipMalloc(reinterpret_cast<void **>(&w.partials), kWsFloats * sizeof(float)) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (hipMalloc(reinterpret_cast<void **>(&w.counters), kWsCounters * sizeof(int)) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(w.partials);
+        return nullptr;
+    }
+    hipLaunchKernelGGL(zero_ints, dim3((kWsCounters + 255) / 256), dim3(256), 0, stream, w.counters, kWsCounters);
+    if (hipGetLastError() != hipSuccess) {
+        (void)hipFree(w.partials);
+        (void)hipFree(w.counters);
+        return nullptr;
+    }
+    return &g_ws.emplace(key, w).first->second;
+}
+
+// Split factor for the band kernel: enough workgroups to cover the CUs twice,
+// at least one 16-row chunk per wave, within the workspace.
+int band_splits(int M, int N, int K, int mb) {
+    const long long bands = (N + kBandCols - 1) / kBandCols;
+    const long long yb = (M + 16 * mb - 1) / (16 * mb);
+    const long long tiles = bands * yb;
+    long long S = (2 * kNumCus + tiles - 1) / tiles;
+    const int waves = mb == 1 ? band_waves<1>() : band_waves<2>();
+    const long long max_by_k = (K + 16 * waves - 1) / (16 * waves);
+    if (S > max_by_k) S = max_by_k;
+    if (S > kMaxSplits) S = kMaxSplits;
+    const long long per_split = 16LL * mb * kBandCols;
+    while (S > 1 && tiles * S * per_split > (long long)kWsFloats) --S;
+    if (tiles > kWsCounters) S = 1;
+    return S < 1 ? 1 : (int)S;
+}
+
+template <int MB, bool TA, bool TB>
+hipError_t launch_band_t(const SplitArgs &sa, hipStream_t stream) {
+    const int bands = (sa.g.N + kBandCols - 1) / kBandCols;
+    dim3 grid((unsigned)(bands * sa.splits), (unsigned)((sa.g.M + 16 * MB - 1) / (16 * MB)));
+    hipLaunchKernelGGL((sgemm_skinny_band<MB, TA, TB>), grid, dim3(64 * band_waves<MB>()), 0, stream, sa);
+    return hipGetLastError();
+}
+
+template <int MB>
+hipError_t launch_band_mb(bool ta, bool tb, const SplitArgs &sa, hipStream_t stream) {
+    if (!ta && !tb) return launch_band_t<MB, false, false>(sa, stream);
+    if (!ta && tb) return launch_band_t<MB, false, true>(sa, stream);
+    if (ta && !tb) return launch_band_t<MB, true, false>(sa, stream);
+    return launch_band_t<MB, true, true>(sa, stream);
+}
+
+hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) {
+    const int mb = g.M <= 16 ? 1 : 2;
+    SplitArgs sa;
+    sa.g = g;
+    sa.ws = nullptr;
+    sa.counters = nullptr;
+    int S = band_splits(g.M, g.N, g.K, mb);
+    if (S > 1) {
+        const Workspace *w = get_workspace(stream);
+        if (w == nullptr) {
+            S = 1;
+        } else {
+            sa.ws = w->partials;
+            sa.counters = w->counters;
+        }
+    }
+    int rps = (((g.K + 15) / 16 + S - 1) / S) * 16;
+    S = (g.K + rps - 1) / rps;
+    if (S < 1) S = 1;
+    sa.splits = S;
+    sa.rows_per_split = rps;
+    if (mb == 1) return launch_band_mb<1>(ta, tb, sa, stream);
+    return launch_band_mb<2>(ta, tb, sa, stream);
 }
 
 template <int MB, bool TA, bool TB>
@@ -647,12 +995,14 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     g.vec_c = aligned16(C) && ldc % 4 == 0;
     const bool ta = op_t(transA), tb = op_t(transB);
     if (config < 0) config = select_config(transA, transB, M, N, K);
-    if (config == kSkinnyConfig && (M + 2 * 16 - 1) / (2 * 16) > 65535) return MISGEMM_TOO_LARGE;
+    if ((config == kSkinnyConfig || config == kBandConfig) && (M + 2 * 16 - 1) / (2 * 16) > 65535)
+        return MISGEMM_TOO_LARGE;
     hipError_t err;
     switch (config) {
         case 0: err = launch_cfg<CfgL>(ta, tb, g, stream); break;
         case 1: err = launch_cfg<CfgS>(ta, tb, g, stream); break;
-        default: err = launch_skinny(ta, tb, g, stream); break;
+        case kSkinnyConfig: err = launch_skinny(ta, tb, g, stream); break;
+        default: err = launch_band(ta, tb, g, stream); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }

@@ -161,6 +161,77 @@ def test_skinny_rows_every_op(ta, tb, M):
     compare(ucase, run_gpu(ucase, inp), run_oracle(ucase, inp), False)
 
 
+BAND = mg.config_names().index("skinny_mfma16_band128_splitk")
+
+
+@pytest.mark.parametrize("ta,tb", OPS)
+@pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (7, 1000, 3001), (32, 130, 17), (17, 4096, 2048),
+                                   (1, 65, 100000), (24, 640, 640)])
+def test_band_split_k(ta, tb, M, N, K):
+    """Split-K band kernel: integer inputs bit-exact, whatever the split."""
+    case = W.Case(f"band_{ta}{tb}_{M}x{N}x{K}", ta, tb, M, N, K, 1.0, -1.0, seed=50 + M, fill="int_rand")
+    note(case.name)
+    inp = W.make_inputs(case)
+    compare(case, run_gpu(case, inp, config=BAND), run_oracle(case, inp), True)
+
+
+def test_band_reduction_is_deterministic():
+    """Twenty back-to-back calls of the split reduction give identical bits."""
+    case = W.C5B.with_(beta=0.0)
+    inp = W.make_inputs(case)
+    A = torch.from_numpy(inp.A).cuda()
+    B = torch.from_numpy(inp.B).cuda()
+    outs = [torch.empty(case.M, case.N, device="cuda") for _ in range(20)]
+    for C in outs:
+        mg.sgemm("N", "N", 1.0, A, B, 0.0, C, config=BAND)
+    torch.cuda.synchronize()
+    ref = outs[0].cpu().numpy()
+    compare(case, ref, run_oracle(case, inp), False)
+    for C in outs[1:]:
+        assert np.array_equal(C.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_band_workspace_reuse_alternating_inputs():
+    """Back-to-back split calls on one stream with different data each time:
+    a partial left from the previous call must never reach the result."""
+    cases = [W.Case(f"alt{i}", "N", "N", 16, 4096, 4096, 1.0, 0.0, seed=60 + i, fill="int_rand") for i in range(2)]
+    inputs = [W.make_inputs(c) for c in cases]
+    wants = [run_oracle(c, i) for c, i in zip(cases, inputs)]
+    dev = [(torch.from_numpy(i.A).cuda(), torch.from_numpy(i.B).cuda()) for i in inputs]
+    outs = []
+    for rep in range(10):
+        A, B = dev[rep % 2]
+        C = torch.empty(16, 4096, device="cuda")
+        mg.sgemm("N", "N", 1.0, A, B, 0.0, C, config=BAND)
+        outs.append(C)
+    torch.cuda.synchronize()
+    for rep, C in enumerate(outs):
+        compare(cases[rep % 2], C.cpu().numpy(), wants[rep % 2], True)
+
+
+def test_band_concurrent_streams():
+    """Two streams run split reductions at once; each has its own workspace."""
+    case = W.C5B.with_(beta=0.0)
+    inp = W.make_inputs(case)
+    want = run_oracle(case, inp)
+    A = torch.from_numpy(inp.A).cuda()
+    B = torch.from_numpy(inp.B).cuda()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(6):
+        for st in (s1, s2):
+            C = torch.empty(case.M, case.N, device="cuda")
+            C.record_stream(st)
+            mg.sgemm("N", "N", 1.0, A, B, 0.0, C, stream=st.cuda_stream, config=BAND)
+            outs.append(C)
+    torch.cuda.synchronize()
+    for C in outs:
+        compare(case, C.cpu().numpy(), want, False)
+    ref = outs[0].cpu().numpy().view(np.uint32)
+    assert all(np.array_equal(C.cpu().numpy().view(np.uint32), ref) for C in outs)
+
+
 # --- every kernel configuration on ragged shapes ------------------------------------------
 
 def _edge_triples(count, seed):
