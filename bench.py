@@ -81,32 +81,33 @@ class Problem:
             self.sets.append((A, B, C))
         torch.cuda.synchronize()
 
-    def call(self, i=0, stream=None):
+    def call(self, i=0, stream=None, config=None):
         import fp32_gemm_nn_amd as mg
 
         c = self.case
         A, B, C = self.sets[i % len(self.sets)]
-        rc = mg.mi_sgemm(c.transA, c.transB, c.M, c.N, c.K, c.alpha, A.data_ptr(), c.lda_,
-                         B.data_ptr(), c.ldb_, c.beta, C.data_ptr(), c.ldc_, stream)
+        args = (c.transA, c.transB, c.M, c.N, c.K, c.alpha, A.data_ptr(), c.lda_,
+                B.data_ptr(), c.ldb_, c.beta, C.data_ptr(), c.ldc_, stream)
+        rc = mg.mi_sgemm(*args) if config is None else mg.mi_sgemm_with_config(config, *args)
         if rc != 0:
             raise RuntimeError(f"mi_sgemm: {mg.mi_sgemm_status_string(rc)}")
 
 
-def time_problem(prob, steps, warmup):
+def time_problem(prob, steps, warmup, config=None):
     """Wall time and HIP-event time of `steps` back-to-back calls on one stream."""
     import torch
 
     stream = torch.cuda.current_stream()
     handle = stream.cuda_stream
     for i in range(warmup):
-        prob.call(i, handle)
+        prob.call(i, handle, config)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(steps):
-        prob.call(i, handle)
+        prob.call(i, handle, config)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -218,6 +219,32 @@ def run_table(path, steps, warmup):
             del prob
 
 
+def run_config_sweep(path, warmup=3):
+    """Every kernel configuration on every workload (one JSON object per line):
+    the data the shape-class rule in select_config is chosen from."""
+    import fp32_gemm_nn_amd as mg
+    from synthetic import workloads as W
+
+    cases = [W.C1, W.C2, *[W.c3(n) for n in W.C3_SIZES], W.C4, *W.C5A, W.C5B]
+    names = mg.config_names()
+    with open(path, "w") as out:
+        for case in cases:
+            skinny = case is W.C5B
+            prob = Problem(case, copies=8 if skinny else 1)
+            chosen = mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)
+            for cfg, name in enumerate(names):
+                if "skinny" in name and case.M > 64:
+                    continue
+                n = 200 if skinny else max(10, min(2000, int(2e-1 / max(case.flops / 100e12, 1e-6))))
+                _, ev = time_problem(prob, n, warmup, config=cfg)
+                per = ev / n
+                row = {"workload": case.name, "config": name, "chosen": cfg == chosen,
+                       "us_per_call": round(per * 1e6, 3), "TFLOPS": round(tflops(case.flops, per), 3)}
+                out.write(json.dumps(row) + "\n")
+                out.flush()
+            del prob
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +253,8 @@ def main():
     ap.add_argument("--mode", choices=["gemm", "copy"], default="gemm")
     ap.add_argument("--table", metavar="PATH", help="also write per-workload numbers to PATH")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--sweep-configs", metavar="PATH",
+                    help="also time every kernel configuration on every workload, to PATH")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -293,6 +322,8 @@ def main():
     del prob
     if args.table:
         run_table(args.table, 20, 5)
+    if args.sweep_configs:
+        run_config_sweep(args.sweep_configs)
     if not args.no_cpu:
         cb = cpu_baseline(case)
         cb.update(host_info())

@@ -73,13 +73,21 @@ struct GemmArgs {
     int vec_c;    // C: 16-byte aligned base, ldc multiple of 4
 };
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+// BM x BN x BK macro tile; WAVES_M x WAVES_N waves share each k-tile; KG such
+// groups of waves take alternate k-tiles (split-K inside the workgroup), each
+// with its own LDS buffers, and are summed at the end in group order.
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
-    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KG = KG_;
+    static constexpr int NTG = 64 * WAVES_M * WAVES_N;   // threads per k-group
+    static constexpr int NT = NTG * KG;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
+    // Waves per SIMD the register allocation must allow: at least two (two
+    // workgroups per CU where LDS allows), more when one workgroup alone
+    // places more than two waves on each SIMD.
+    static constexpr int WAVES_PER_EU = NT / 256 > 2 ? NT / 256 : 2;
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
 };
@@ -206,34 +214,130 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, i
     tn = in_g / gsz;
 }
 
+// MFMA operands of one q-group (four consecutive k-steps of a k-tile) for one
+// wave: a[blk][e] and b[blk][e] feed step e of the 32x32x2 MFMA for block blk.
 template <class CFG, bool TA, bool TB>
-__global__ __launch_bounds__(CFG::NT) void sgemm_mfma32(GemmArgs g) {
-    constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NT = CFG::NT;
+struct Frag {
+    static constexpr int FM = CFG::FM, FN = CFG::FN, WTM = CFG::WTM, WTN = CFG::WTN, HB = CFG::BK / 2;
+    float a[FM][4];
+    float b[FN][4];
+
+    // as/bs: LDS tiles of one k-tile, row strides AS/BS.
+    template <int AS, int BS>
+    __device__ __forceinline__ void read(const float *as, const float *bs, int q, int wm, int wn, int li, int lh) {
+        if (!TA) {
+            // k-contiguous A tile [m][k]: block blk, lane row li is m = 32*blk + li.
+#pragma unroll
+            for (int blk = 0; blk < FM; ++blk)
+                LdsVec<4>::get(as + (wm * WTM + 32 * blk + li) * AS + lh * HB + 4 * q, a[blk]);
+        } else {
+            // m-contiguous A tile [k][m]: block blk, lane row li is m = FM*li + blk.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float t[FM];
+                LdsVec<FM>::get(as + (lh * HB + 4 * q + e) * AS + wm * WTM + FM * li, t);
+#pragma unroll
+                for (int blk = 0; blk < FM; ++blk) a[blk][e] = t[blk];
+            }
+        }
+        if (TB) {
+            // k-contiguous B tile [n][k]: block blk, lane column li is n = 32*blk + li.
+#pragma unroll
+            for (int blk = 0; blk < FN; ++blk)
+                LdsVec<4>::get(bs + (wn * WTN + 32 * blk + li) * BS + lh * HB + 4 * q, b[blk]);
+        } else {
+            // n-contiguous B tile [k][n]: block blk, lane column li is n = FN*li + blk.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float t[FN];
+                LdsVec<FN>::get(bs + (lh * HB + 4 * q + e) * BS + wn * WTN + FN * li, t);
+#pragma unroll
+                for (int blk = 0; blk < FN; ++blk) b[blk][e] = t[blk];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void mma(f32x16 (&acc)[FM][FN]) const {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+    }
+};
+
+// Instruction-order hints for the straight-line k-tile iteration (one
+// scheduling region ending at the barrier): the next tile's global loads are
+// spread over the first MFMAs, each q-group's fragment reads for the next
+// group over the MFMAs of the current one, and the LDS writes of the next
+// tile over the last group. Masks: 0x008 MFMA, 0x020 VMEM read, 0x100 DS read,
+// 0x200 DS write.
+template <int MASK, int N>
+__device__ __forceinline__ void hint_pairs() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(MASK, 1, 0);
+    }
+}
+
+template <int MFMA_PER_Q, int Q, int GLOADS, int DSREADS, int DSWRITES, int q = 0>
+__device__ __forceinline__ void schedule_iteration() {
+    if constexpr (GLOADS + DSREADS <= MFMA_PER_Q && DSWRITES <= MFMA_PER_Q && q < Q) {
+        constexpr int gl = q == 0 ? GLOADS : 0;
+        constexpr int dr = q + 1 < Q ? DSREADS : 0;
+        constexpr int dw = q + 1 < Q ? 0 : DSWRITES;
+        hint_pairs<0x020, gl>();
+        hint_pairs<0x100, dr>();
+        hint_pairs<0x200, dw>();
+        __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER_Q - gl - dr - dw, 0);
+        schedule_iteration<MFMA_PER_Q, Q, GLOADS, DSREADS, DSWRITES, q + 1>();
+    }
+}
+
+template <class CFG, bool TA, bool TB>
+__global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES_PER_EU)))
+void sgemm_mfma32(GemmArgs g) {
+    constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NTG = CFG::NTG, KG = CFG::KG;
     constexpr int FM = CFG::FM, FN = CFG::FN, WTM = CFG::WTM, WTN = CFG::WTN;
-    constexpr int HB = BK / 2;
+    constexpr int Q = BK / 8;                   // q-groups per k-tile
+    static_assert(Q % 2 == 0, "fragment buffers alternate, so the q-group count must be even");
     // Stored tile shapes: A is BM x BK ('N', k contiguous) or BK x BM ('T',
     // m contiguous); B is BK x BN ('N', n contiguous) or BN x BK ('T').
-    using ACopy = TileCopy<TA ? BK : BM, TA ? BM : BK, NT>;
-    using BCopy = TileCopy<TB ? BN : BK, TB ? BK : BN, NT>;
+    using ACopy = TileCopy<TA ? BK : BM, TA ? BM : BK, NTG>;
+    using BCopy = TileCopy<TB ? BN : BK, TB ? BK : BN, NTG>;
+    using F = Frag<CFG, TA, TB>;
     constexpr int A_FLOATS = ACopy::LDS_FLOATS, B_FLOATS = BCopy::LDS_FLOATS;
     constexpr int AS = ACopy::STRIDE, BS = BCopy::STRIDE;
+    constexpr int GROUP_FLOATS = 2 * (A_FLOATS + B_FLOATS);
+    // The k-group reduction reuses the tile buffers: KG-1 groups x waves x
+    // FM*FN accumulator blocks x 16 registers x 64 lanes.
+    constexpr int RED_FLOATS = (KG - 1) * (NTG / 64) * FM * FN * 16 * 64;
+    static_assert(RED_FLOATS <= KG * GROUP_FLOATS, "reduction does not fit the tile buffers");
 
-    __shared__ __attribute__((aligned(16))) float lds[2 * (A_FLOATS + B_FLOATS)];
-    // Buffer i of A at lds + i*A_FLOATS, of B at lds + 2*A_FLOATS + i*B_FLOATS.
-    float *const a_lds = lds;
-    float *const b_lds = lds + 2 * A_FLOATS;
+    __shared__ __attribute__((aligned(16))) float lds[KG * GROUP_FLOATS];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int grp = tid / NTG, gtid = tid % NTG;     // k-group and thread within it
+    const int lane = gtid & 63, wave = gtid >> 6;
     const int li = lane & 31, lh = lane >> 5;
     const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
+    // This group's buffer i of A at a_lds + i*A_FLOATS, of B at b_lds + i*B_FLOATS.
+    float *const a_lds = lds + grp * GROUP_FLOATS;
+    float *const b_lds = a_lds + 2 * A_FLOATS;
 
     int tm, tn;
     tile_coords(g.tiles_m, g.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
-    const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
     const bool vec = g.vec_ab != 0;
+    // Interior workgroup: every complete k-tile can be fetched unguarded.
+    const bool wg_fast = (m0 + BM <= M) && (n0 + BN <= N) && vec;
+    const int kfull = K / BK;
+    const int ktiles = (K + BK - 1) / BK;
+    const int rounds = (ktiles + KG - 1) / KG;
 
     // Base of the tile at k = 0 in each stored matrix, and the per-k-tile step.
     const float *a_ptr = TA ? g.A + m0 : g.A + (size_t)m0 * g.lda;
@@ -245,103 +349,130 @@ __global__ __launch_bounds__(CFG::NT) void sgemm_mfma32(GemmArgs g) {
 
     ACopy ca;
     BCopy cb;
-    const int ktiles = (K + BK - 1) / BK;
-
-    auto fetch = [&](int kt) {
+    auto fetch_fast = [&](int kt) {
+        ca.load(a_ptr + kt * a_step, g.lda, 0, 0, false, true, gtid);
+        cb.load(b_ptr + kt * b_step, g.ldb, 0, 0, false, true, gtid);
+    };
+    auto fetch_any = [&](int kt) {
         const int k0 = kt * BK;
-        const bool guard = !(full_mn && vec && k0 + BK <= K);
+        const bool guard = !(wg_fast && kt < kfull);
         // Rows/cols left counted from this k-tile's origin.
         ca.load(a_ptr + kt * a_step, g.lda, TA ? a_rows - k0 : a_rows, TA ? a_cols : a_cols - k0,
-                guard, vec, tid);
+                guard, vec, gtid);
         cb.load(b_ptr + kt * b_step, g.ldb, TB ? b_rows : b_rows - k0, TB ? b_cols - k0 : b_cols,
-                guard, vec, tid);
+                guard, vec, gtid);
     };
 
     f32x16 acc[FM][FN];
 #pragma unroll
-    for (int a = 0; a < FM; ++a)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int b = 0; b < FN; ++b)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    fetch(0);
-    ca.store(a_lds, tid);
-    cb.store(b_lds, tid);
+    // Group grp takes k-tiles grp, grp + KG, ... In round r its k-tile is
+    // t = r*KG + grp. Invariant at the top of round r: the group's LDS buffer
+    // r&1 holds k-tile t (when t < ktiles) and f0 holds its q-group 0.
+    F f0, f1;
+    if (grp < ktiles) {
+        fetch_any(grp);
+        ca.store(a_lds, gtid);
+        cb.store(b_lds, gtid);
+    }
     __syncthreads();
+    if (grp < ktiles) f0.template read<AS, BS>(a_lds, b_lds, 0, wm, wn, li, lh);
 
-    for (int kt = 0; kt < ktiles; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < ktiles) fetch(kt + 1);
-
+    for (int r = 0; r < rounds; ++r) {
+        const int t = r * KG + grp, tn_ = t + KG;
+        const int cur = r & 1, nxt = cur ^ 1;
         const float *as = a_lds + cur * A_FLOATS;
         const float *bs = b_lds + cur * B_FLOATS;
+        float *as_n = a_lds + nxt * A_FLOATS;
+        float *bs_n = b_lds + nxt * B_FLOATS;
+        if (wg_fast && tn_ < kfull) {
+            // Straight-line round: this and the next k-tile are complete and in range.
+            fetch_fast(tn_);
 #pragma unroll
-        for (int q = 0; q < BK / 8; ++q) {
-            float af[FM][4], bf[FN][4];
-            if (!TA) {
-                // k-contiguous A tile [m][k]: block a, lane row li is m = 32a + li.
-#pragma unroll
-                for (int a = 0; a < FM; ++a) {
-                    const float *p = as + (wm * WTM + 32 * a + li) * AS + lh * HB + 4 * q;
-                    LdsVec<4>::get(p, af[a]);
+            for (int q = 0; q < Q; q += 2) {
+                f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
+                f0.mma(acc);
+                if (q + 2 < Q) {
+                    f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
+                } else {
+                    ca.store(as_n, gtid);
+                    cb.store(bs_n, gtid);
                 }
-            } else {
-                // m-contiguous A tile [k][m]: block a, lane row li is m = FM*li + a.
+                f1.mma(acc);
+            }
+            // DS reads per q-group: FM (or FN) 16-byte reads of a k-contiguous
+            // tile, four narrow reads of an m/n-contiguous one.
+            schedule_iteration<4 * FM * FN, Q, ACopy::PER_THREAD + BCopy::PER_THREAD,
+                               (TA ? 4 : FM) + (TB ? FN : 4), ACopy::PER_THREAD + BCopy::PER_THREAD>();
+            __syncthreads();
+            f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
+        } else {
+            const bool has_cur = t < ktiles, has_next = tn_ < ktiles;
+            if (has_next) fetch_any(tn_);
+            if (has_cur) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float t[FM];
-                    LdsVec<FM>::get(as + (lh * HB + 4 * q + e) * AS + wm * WTM + FM * li, t);
-#pragma unroll
-                    for (int a = 0; a < FM; ++a) af[a][e] = t[a];
+                for (int q = 0; q < Q; q += 2) {
+                    f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
+                    f0.mma(acc);
+                    if (q + 2 < Q) f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
+                    f1.mma(acc);
                 }
             }
-            if (TB) {
-                // k-contiguous B tile [n][k]: block b, lane column li is n = 32b + li.
-#pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const float *p = bs + (wn * WTN + 32 * b + li) * BS + lh * HB + 4 * q;
-                    LdsVec<4>::get(p, bf[b]);
-                }
-            } else {
-                // n-contiguous B tile [k][n]: block b, lane column li is n = FN*li + b.
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float t[FN];
-                    LdsVec<FN>::get(bs + (lh * HB + 4 * q + e) * BS + wn * WTN + FN * li, t);
-#pragma unroll
-                    for (int b = 0; b < FN; ++b) bf[b][e] = t[b];
-                }
+            if (has_next) {
+                ca.store(as_n, gtid);
+                cb.store(bs_n, gtid);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int a = 0; a < FM; ++a)
-#pragma unroll
-                    for (int b = 0; b < FN; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a][e], bf[b][e], acc[a][b],
-                                                                         0, 0, 0);
+            __syncthreads();
+            if (has_next) f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
         }
-
-        if (kt + 1 < ktiles) {
-            ca.store(a_lds + (cur ^ 1) * A_FLOATS, tid);
-            cb.store(b_lds + (cur ^ 1) * B_FLOATS, tid);
-        }
-        __syncthreads();
     }
 
-    // Epilogue. Accumulator element r of block (a, b) in lane (li, lh) is
+    if constexpr (KG > 1) {
+        // Groups 1..KG-1 hand their accumulators to group 0 through LDS (the
+        // tile buffers are free after the last barrier); group 0 adds them in
+        // group order, so the sum is the same on every call.
+        constexpr int SLOT = FM * FN * 16 * 64;            // floats per wave
+        constexpr int WAVES = NTG / 64;
+        if (grp > 0) {
+            float *dst = lds + ((grp - 1) * WAVES + wave) * SLOT + lane;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g2 = 1; g2 < KG; ++g2) {
+            const float *src = lds + ((g2 - 1) * WAVES + wave) * SLOT + lane;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
+        }
+    }
+
+    // Epilogue. Accumulator element r of block (i, j) in lane (li, lh) is
     // block row 8*(r/4) + 4*lh + r%4, block column li.
     const float alpha = g.alpha, beta = g.beta;
     float *const cw = g.C + (size_t)(m0 + wm * WTM) * g.ldc + (n0 + wn * WTN);
     const int rows_left = M - (m0 + wm * WTM), cols_left = N - (n0 + wn * WTN);
     const int ldc = g.ldc;
 #pragma unroll
-    for (int a = 0; a < FM; ++a) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int ib = 8 * (r / 4) + 4 * lh + (r % 4);
-            const int row = TA ? FM * ib + a : 32 * a + ib;
+            const int row = TA ? FM * ib + i : 32 * i + ib;
             if (row >= rows_left) continue;
             float *crow = cw + (size_t)row * ldc;
             if (!TB) {
@@ -349,15 +480,15 @@ __global__ __launch_bounds__(CFG::NT) void sgemm_mfma32(GemmArgs g) {
                 const int col = FN * li;
                 float out[FN];
 #pragma unroll
-                for (int b = 0; b < FN; ++b) out[b] = alpha * acc[a][b][r];
+                for (int j = 0; j < FN; ++j) out[j] = alpha * acc[i][j][r];
                 store_run<FN>(crow + col, out, beta, g.vec_c && col + FN <= cols_left, cols_left - col);
             } else {
 #pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const int col = 32 * b + li;
+                for (int j = 0; j < FN; ++j) {
+                    const int col = 32 * j + li;
                     if (col < cols_left) {
                         float *p = crow + col;
-                        const float o = alpha * acc[a][b][r];
+                        const float o = alpha * acc[i][j][r];
                         *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
                     }
                 }
@@ -767,8 +898,11 @@ __global__ __launch_bounds__(256) void scale_c(float *C, int M, int N, int ldc, 
 // ---------------------------------------------------------------------------
 // Configuration table.
 
-using CfgL = TileCfg<128, 128, 32, 2, 2>;   // 4 waves, 64 x 64 per wave
-using CfgS = TileCfg<64, 64, 32, 2, 2>;     // 4 waves, 32 x 32 per wave
+using CfgL = TileCfg<128, 128, 32, 2, 2>;        // 4 waves, 64 x 64 per wave
+using CfgS = TileCfg<64, 64, 32, 2, 2>;          // 4 waves, 32 x 32 per wave
+using CfgS2 = TileCfg<64, 64, 32, 2, 2, 2>;      // 8 waves: 2 k-groups of 4
+using CfgS4 = TileCfg<64, 64, 32, 2, 2, 4>;      // 16 waves: 4 k-groups of 4
+using CfgL2 = TileCfg<128, 128, 32, 2, 2, 2>;    // 8 waves: 2 k-groups of 4
 
 struct ConfigInfo {
     const char *name;
@@ -780,6 +914,9 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_64x64x32_w2x2", CfgS::BM, CfgS::BN, CfgS::NT},
     {"skinny_mfma16_16cols_splitk8", 32, 16, 64 * kSkinnyWaves},
     {"skinny_mfma16_band128_splitk", 32, kBandCols, 64 * kBandWaves},
+    {"mfma32_64x64x32_w2x2_kg2", CfgS2::BM, CfgS2::BN, CfgS2::NT},
+    {"mfma32_64x64x32_w2x2_kg4", CfgS4::BM, CfgS4::BN, CfgS4::NT},
+    {"mfma32_128x128x32_w2x2_kg2", CfgL2::BM, CfgL2::BN, CfgL2::NT},
 };
 constexpr int kSkinnyConfig = 2;
 constexpr int kBandConfig = 3;
@@ -810,14 +947,33 @@ int check_args(char transA, char transB, int M, int N, int K, float alpha, const
     return MISGEMM_SUCCESS;
 }
 
+// Fraction of the busiest CU's tile slots that hold work when `tiles`
+// workgroups are spread over the CUs: 1 when every CU gets the same count.
+double cu_balance(long long tiles) {
+    const long long per_cu = (tiles + kNumCus - 1) / kNumCus;
+    return (double)tiles / (double)(per_cu * kNumCus);
+}
+
+// Shape class -> configuration, from per-configuration timings of the square
+// sweep, the layer shapes and the ragged shape on MI355X:
+//   M <= 32                      skinny band kernel (HBM-bound);
+//   >= 256 tiles of 128 x 128    128 x 128, unless 64 x 64 tiles spread more
+//                                evenly over the CUs by more than the 64 x 64
+//                                kernel's lower per-tile efficiency (0.87);
+//   192..255 such tiles          128 x 128 with two k-groups (8 waves);
+//   else, by 64 x 64 tiles:      >= 512 plain, > 256 two k-groups, else four.
 int select_config(char transA, char transB, int M, int N, int K) {
     (void)transA;
     (void)transB;
     (void)K;
     if (M <= kSkinnyMaxM) return kBandConfig;
     const long long tiles_l = (long long)((M + CfgL::BM - 1) / CfgL::BM) * ((N + CfgL::BN - 1) / CfgL::BN);
-    if (tiles_l >= kNumCus) return 0;
-    return 1;
+    const long long tiles_s = (long long)((M + CfgS::BM - 1) / CfgS::BM) * ((N + CfgS::BN - 1) / CfgS::BN);
+    if (tiles_l >= kNumCus) return 0.87 * cu_balance(tiles_s) > cu_balance(tiles_l) ? 1 : 0;
+    if (tiles_l >= 3 * kNumCus / 4) return 6;
+    if (tiles_s >= 2 * kNumCus) return 1;
+    if (tiles_s > kNumCus) return 4;
+    return 5;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1002,7 +1158,10 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case 0: err = launch_cfg<CfgL>(ta, tb, g, stream); break;
         case 1: err = launch_cfg<CfgS>(ta, tb, g, stream); break;
         case kSkinnyConfig: err = launch_skinny(ta, tb, g, stream); break;
-        default: err = launch_band(ta, tb, g, stream); break;
+        case kBandConfig: err = launch_band(ta, tb, g, stream); break;
+        case 4: err = launch_cfg<CfgS2>(ta, tb, g, stream); break;
+        case 5: err = launch_cfg<CfgS4>(ta, tb, g, stream); break;
+        default: err = launch_cfg<CfgL2>(ta, tb, g, stream); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }

@@ -112,8 +112,15 @@ def test_shape_class_selection():
     # 4096^2 output: 1024 tiles of 128 x 128, enough to fill 256 CUs.
     assert "128x128" in sel("N", "N", 4096, 4096, 4096)
     assert "128x128" in sel("T", "T", 2048, 4096, 1024)
-    # 1024^2 output: 64 such tiles only, so smaller tiles.
-    assert "128x128" not in sel("N", "N", 1024, 1024, 1024)
+    # 1024^2 output: 64 such tiles only, so smaller tiles with four k-groups.
+    assert sel("N", "N", 1024, 1024, 1024) == "mfma32_64x64x32_w2x2_kg4"
+    assert sel("N", "N", 1000, 1300, 700) == "mfma32_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 1792, 1792, 1792) == "mfma32_128x128x32_w2x2_kg2"
+    assert sel("N", "N", 1536, 1536, 1536) == "mfma32_64x64x32_w2x2"
+    # Square sizes where 64 x 64 tiles spread over the 256 CUs more evenly.
+    for n, want in [(2048, "128x128x32_w2x2"), (2304, "64x64x32_w2x2"), (2560, "128x128x32_w2x2"),
+                    (3072, "64x64x32_w2x2"), (3584, "64x64x32_w2x2"), (3840, "128x128x32_w2x2")]:
+        assert sel("N", "N", n, n, n) == "mfma32_" + want, n
     # M <= 32: the skinny, bandwidth-bound kernel.
     assert "skinny" in sel("N", "N", 16, 4096, 4096)
     assert "skinny" in sel("T", "T", 32, 100, 7)
