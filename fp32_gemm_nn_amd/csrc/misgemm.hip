@@ -668,11 +668,15 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void sgemm_skinny16(GemmArgs g) 
 constexpr int kBandCols = 128;
 constexpr int kBandWaves = 8;
 constexpr int kMaxSplits = 32;
-// Waves per workgroup: eight for one row block; four for two, so that each
-// wave may use 512 registers (the two-row-block fragments need ~260).
-template <int MB> constexpr int band_waves() { return MB == 1 ? kBandWaves : kBandWaves / 2; }
-// 16-row chunks per register buffer.
-template <int MB> constexpr int band_chunks() { return 2; }
+// Waves per workgroup. One row block: sixteen on the unguarded path (more
+// loads in flight per CU; its fragments fit 128 registers), eight on the
+// guarded one. Two row blocks: four, so each wave may use 512 registers (the
+// fragments need ~260) and the LDS partial blocks fit.
+template <int MB, bool FAST> constexpr int band_waves() {
+    return MB == 1 ? (FAST ? 2 * kBandWaves : kBandWaves) : kBandWaves / 2;
+}
+// 16-row chunks per register buffer: one with sixteen waves, else two.
+template <int MB, bool FAST> constexpr int band_chunks() { return MB == 1 && FAST ? 1 : 2; }
 
 struct SplitArgs {
     GemmArgs g;
@@ -682,20 +686,36 @@ struct SplitArgs {
     int rows_per_split;   // multiple of 16
 };
 
-template <int MB, bool TA, bool TB>
+template <int MB, bool TA, bool TB, bool FAST>
 struct BandFrag {
-    static constexpr int kBandChunks = band_chunks<MB>();
+    static constexpr int kBandChunks = band_chunks<MB, FAST>();
     f32x4 b[kBandChunks][8];
     float a[kBandChunks][MB][4];
 
-    // Chunk u covers k0 = kc + 16u .. +15, valid below kend.
+    // Chunk u covers k0 = kc + 16u .. +15, valid below kend. FAST: the host
+    // has checked that every band lies inside N, every chunk below kend, all
+    // 16*MB rows of A exist and the pointers allow 16-byte loads, so nothing
+    // is checked per element.
     __device__ __forceinline__ void load(const GemmArgs &g, int m0, int n0, int c, int q, int kc, int kend,
                                          bool vec) {
         const int M = g.M, N = g.N, lda = g.lda, ldb = g.ldb;
 #pragma unroll
         for (int u = 0; u < kBandChunks; ++u) {
             const int kq = kc + 16 * u + 4 * q;
-            if (!TB) {
+            if constexpr (FAST) {
+                if (!TB) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            b[u][4 * h + j] =
+                                *reinterpret_cast<const f32x4 *>(g.B + (size_t)(kq + j) * ldb + n0 + 64 * h + 4 * c);
+                } else {
+#pragma unroll
+                    for (int blk = 0; blk < 8; ++blk)
+                        b[u][blk] = *reinterpret_cast<const f32x4 *>(g.B + (size_t)(n0 + 16 * blk + c) * ldb + kq);
+                }
+            } else if constexpr (!TB) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int col = n0 + 64 * h + 4 * c;
@@ -731,7 +751,14 @@ struct BandFrag {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = m0 + 16 * mb + c;
-                if (!TA && vec && row < M && kq + 3 < kend) {
+                if (FAST && !TA) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a[u][mb][j] = v[j];
+                } else if (FAST) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a[u][mb][j] = g.A[(size_t)(kq + j) * lda + row];
+                } else if (!TA && vec && row < M && kq + 3 < kend) {
                     const f32x4 v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) a[u][mb][j] = v[j];
@@ -763,9 +790,9 @@ struct BandFrag {
     }
 };
 
-template <int MB, bool TA, bool TB>
-__global__ __launch_bounds__(64 * band_waves<MB>()) void sgemm_skinny_band(SplitArgs sa) {
-    constexpr int W = band_waves<MB>();
+template <int MB, bool TA, bool TB, bool FAST>
+__global__ __launch_bounds__((64 * band_waves<MB, FAST>())) void sgemm_skinny_band(SplitArgs sa) {
+    constexpr int W = band_waves<MB, FAST>();
     constexpr int NT = 64 * W;
     constexpr int T = 16 * MB * kBandCols;       // outputs per workgroup
     __shared__ float red[W][T];
@@ -798,9 +825,16 @@ __global__ __launch_bounds__(64 * band_waves<MB>()) void sgemm_skinny_band(Split
 #pragma unroll
         for (int blk = 0; blk < 8; ++blk) acc[mb][blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    constexpr int STEP = 16 * band_chunks<MB>();
-    if (kw0 < kw1) {
-        BandFrag<MB, TA, TB> f0, f1;
+    constexpr int STEP = 16 * band_chunks<MB, FAST>();
+    if (FAST) {
+        // One register buffer: sixteen waves per CU keep enough loads in flight.
+        BandFrag<MB, TA, TB, FAST> f;
+        for (int kc = kw0; kc < kw1; kc += STEP) {
+            f.load(g, m0, n0, c, q, kc, kw1, vec);
+            f.mma(acc);
+        }
+    } else if (kw0 < kw1) {
+        BandFrag<MB, TA, TB, FAST> f0, f1;
         f0.load(g, m0, n0, c, q, kw0, kw1, vec);
         for (int kc = kw0; kc < kw1; kc += 2 * STEP) {
             if (kc + STEP < kw1) f1.load(g, m0, n0, c, q, kc + STEP, kw1, vec);
@@ -823,21 +857,33 @@ __global__ __launch_bounds__(64 * band_waves<MB>()) void sgemm_skinny_band(Split
     __syncthreads();
 
     const float alpha = g.alpha, beta = g.beta;
-    auto finish = [&](int idx, float sum) {
+    // C values of this thread's outputs, loaded now (beta != 0) so that the
+    // workgroup that finishes the band does not wait for them at the end.
+    constexpr int PER = (T + NT - 1) / NT;
+    float c_in[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = tid + NT * i;
+        const int row = m0 + idx / kBandCols, col = n0 + idx % kBandCols;
+        c_in[i] = (beta != 0.0f && idx < T && row < M && col < N) ? g.C[(size_t)row * g.ldc + col] : 0.0f;
+    }
+    auto finish = [&](int i, int idx, float sum) {
         const int row = m0 + idx / kBandCols, col = n0 + idx % kBandCols;
         if (row < M && col < N) {
-            float *p = g.C + (size_t)row * g.ldc + col;
             const float o = alpha * sum;
-            *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
+            g.C[(size_t)row * g.ldc + col] = (beta != 0.0f) ? fmaf(beta, c_in[i], o) : o;
         }
     };
 
     if (S == 1) {
-        for (int idx = tid; idx < T; idx += NT) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + NT * i;
+            if (idx >= T) break;
             float sum = 0.0f;
 #pragma unroll
             for (int v = 0; v < W; ++v) sum += red[v][idx];
-            finish(idx, sum);
+            finish(i, idx, sum);
         }
         return;
     }
@@ -861,21 +907,26 @@ __global__ __launch_bounds__(64 * band_waves<MB>()) void sgemm_skinny_band(Split
         is_last = __hip_atomic_fetch_add(&sa.counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == S - 1;
     __syncthreads();
     if (!is_last) return;
-    // All S loads of an output are issued before any is summed (the sum
-    // itself still runs in split order).
+    // The loads of eight splits are issued before they are summed; the sum
+    // runs in split order.
     const float *parts = sa.ws + (size_t)tile * S * T;
-    for (int idx = tid; idx < T; idx += NT) {
-        float v[kMaxSplits];
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplits; ++sp)
-            v[sp] = sp < S ? __hip_atomic_load(parts + (size_t)sp * T + idx, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_SYSTEM)
-                           : 0.0f;
+    for (int i = 0; i < PER; ++i) {
+        const int idx = tid + NT * i;
+        if (idx >= T) break;
         float sum = 0.0f;
+        for (int sp0 = 0; sp0 < S; sp0 += 8) {
+            const float *p = parts + (size_t)sp0 * T + idx;
+            float v[8];
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplits; ++sp)
-            if (sp < S) sum += v[sp];
-        finish(idx, sum);
+            for (int i = 0; i < 8; ++i)
+                v[i] = sp0 + i < S ? __hip_atomic_load(p + (size_t)i * T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                                   : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (sp0 + i < S) sum += v[i];
+        }
+        finish(i, idx, sum);
     }
     if (tid == 0) __hip_atomic_store(&sa.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
@@ -1027,14 +1078,17 @@ const Workspace *get_workspace(hipStream_t stream) {
     return &g_ws.emplace(key, w).first->second;
 }
 
-// Split factor for the band kernel: enough workgroups to cover the CUs twice,
+// Split factor for the band kernel: enough workgroups to fill every CU's
+// workgroup slots once (the LDS partial blocks limit how many fit on a CU),
 // at least one 16-row chunk per wave, within the workspace.
-int band_splits(int M, int N, int K, int mb) {
+int band_splits(int M, int N, int K, int mb, bool fast) {
     const long long bands = (N + kBandCols - 1) / kBandCols;
     const long long yb = (M + 16 * mb - 1) / (16 * mb);
     const long long tiles = bands * yb;
-    long long S = (2 * kNumCus + tiles - 1) / tiles;
-    const int waves = mb == 1 ? band_waves<1>() : band_waves<2>();
+    const int waves = mb == 1 ? (fast ? band_waves<1, true>() : band_waves<1, false>()) : band_waves<2, false>();
+    const long long lds_bytes = (long long)waves * 16 * mb * kBandCols * 4;
+    const long long per_cu = lds_bytes > 80 * 1024 ? 1 : 2;
+    long long S = (per_cu * kNumCus + tiles - 1) / tiles;
     const long long max_by_k = (K + 16 * waves - 1) / (16 * waves);
     if (S > max_by_k) S = max_by_k;
     if (S > kMaxSplits) S = kMaxSplits;
@@ -1044,20 +1098,20 @@ int band_splits(int M, int N, int K, int mb) {
     return S < 1 ? 1 : (int)S;
 }
 
-template <int MB, bool TA, bool TB>
+template <int MB, bool TA, bool TB, bool FAST>
 hipError_t launch_band_t(const SplitArgs &sa, hipStream_t stream) {
     const int bands = (sa.g.N + kBandCols - 1) / kBandCols;
     dim3 grid((unsigned)(bands * sa.splits), (unsigned)((sa.g.M + 16 * MB - 1) / (16 * MB)));
-    hipLaunchKernelGGL((sgemm_skinny_band<MB, TA, TB>), grid, dim3(64 * band_waves<MB>()), 0, stream, sa);
+    hipLaunchKernelGGL((sgemm_skinny_band<MB, TA, TB, FAST>), grid, dim3((64 * band_waves<MB, FAST>())), 0, stream, sa);
     return hipGetLastError();
 }
 
-template <int MB>
+template <int MB, bool FAST>
 hipError_t launch_band_mb(bool ta, bool tb, const SplitArgs &sa, hipStream_t stream) {
-    if (!ta && !tb) return launch_band_t<MB, false, false>(sa, stream);
-    if (!ta && tb) return launch_band_t<MB, false, true>(sa, stream);
-    if (ta && !tb) return launch_band_t<MB, true, false>(sa, stream);
-    return launch_band_t<MB, true, true>(sa, stream);
+    if (!ta && !tb) return launch_band_t<MB, false, false, FAST>(sa, stream);
+    if (!ta && tb) return launch_band_t<MB, false, true, FAST>(sa, stream);
+    if (ta && !tb) return launch_band_t<MB, true, false, FAST>(sa, stream);
+    return launch_band_t<MB, true, true, FAST>(sa, stream);
 }
 
 hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) {
@@ -1066,7 +1120,10 @@ hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) 
     sa.g = g;
     sa.ws = nullptr;
     sa.counters = nullptr;
-    int S = band_splits(g.M, g.N, g.K, mb);
+    // Unguarded instantiation: whole bands, whole 16-row chunks, whole row
+    // blocks, 16-byte loads (one row block only).
+    const bool fast = mb == 1 && g.vec_ab && g.N % kBandCols == 0 && g.K % 16 == 0 && g.M % 16 == 0;
+    int S = band_splits(g.M, g.N, g.K, mb, fast);
     if (S > 1) {
         const Workspace *w = get_workspace(stream);
         if (w == nullptr) {
@@ -1081,8 +1138,8 @@ hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) 
     if (S < 1) S = 1;
     sa.splits = S;
     sa.rows_per_split = rps;
-    if (mb == 1) return launch_band_mb<1>(ta, tb, sa, stream);
-    return launch_band_mb<2>(ta, tb, sa, stream);
+    if (mb == 1) return fast ? launch_band_mb<1, true>(ta, tb, sa, stream) : launch_band_mb<1, false>(ta, tb, sa, stream);
+    return launch_band_mb<2, false>(ta, tb, sa, stream);
 }
 
 template <int MB, bool TA, bool TB>
