@@ -76,7 +76,7 @@ struct GemmArgs {
 // BM x BN x BK macro tile; WAVES_M x WAVES_N waves share each k-tile; KG such
 // groups of waves take alternate k-tiles (split-K inside the workgroup), each
 // with its own LDS buffers, and are summed at the end in group order.
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1, int EU_ = 0>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KG = KG_;
@@ -87,7 +87,7 @@ struct TileCfg {
     // Waves per SIMD the register allocation must allow: at least two (two
     // workgroups per CU where LDS allows), more when one workgroup alone
     // places more than two waves on each SIMD.
-    static constexpr int WAVES_PER_EU = NT / 256 > 2 ? NT / 256 : 2;
+    static constexpr int WAVES_PER_EU = EU_ ? EU_ : (NT / 256 > 2 ? NT / 256 : 2);
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
 };
@@ -283,10 +283,31 @@ __device__ __forceinline__ void hint_pairs() {
     }
 }
 
+// Global loads of the next tile per q-group: all in the first group when they
+// fit beside its fragment reads, else spread over the groups before the last.
+template <int MFMA_PER_Q, int Q, int GLOADS, int DSREADS>
+constexpr int gloads_in_group(int q) {
+    if (GLOADS + DSREADS <= MFMA_PER_Q) return q == 0 ? GLOADS : 0;
+    const int per = (GLOADS + Q - 2) / (Q - 1);
+    const int before = per * q;
+    if (q >= Q - 1 || before >= GLOADS) return 0;
+    return GLOADS - before < per ? GLOADS - before : per;
+}
+
+template <int MFMA_PER_Q, int Q, int GLOADS, int DSREADS, int DSWRITES>
+constexpr bool hints_fit() {
+    if (DSWRITES > MFMA_PER_Q || Q < 2) return false;
+    for (int q = 0; q + 1 < Q; ++q)
+        if (gloads_in_group<MFMA_PER_Q, Q, GLOADS, DSREADS>(q) + DSREADS > MFMA_PER_Q) return false;
+    int total = 0;
+    for (int q = 0; q < Q; ++q) total += gloads_in_group<MFMA_PER_Q, Q, GLOADS, DSREADS>(q);
+    return total == GLOADS;
+}
+
 template <int MFMA_PER_Q, int Q, int GLOADS, int DSREADS, int DSWRITES, int q = 0>
 __device__ __forceinline__ void schedule_iteration() {
-    if constexpr (GLOADS + DSREADS <= MFMA_PER_Q && DSWRITES <= MFMA_PER_Q && q < Q) {
-        constexpr int gl = q == 0 ? GLOADS : 0;
+    if constexpr (hints_fit<MFMA_PER_Q, Q, GLOADS, DSREADS, DSWRITES>() && q < Q) {
+        constexpr int gl = gloads_in_group<MFMA_PER_Q, Q, GLOADS, DSREADS>(q);
         constexpr int dr = q + 1 < Q ? DSREADS : 0;
         constexpr int dw = q + 1 < Q ? 0 : DSWRITES;
         hint_pairs<0x020, gl>();
@@ -954,6 +975,10 @@ using CfgS = TileCfg<64, 64, 32, 2, 2>;          // 4 waves, 32 x 32 per wave
 using CfgS2 = TileCfg<64, 64, 32, 2, 2, 2>;      // 8 waves: 2 k-groups of 4
 using CfgS4 = TileCfg<64, 64, 32, 2, 2, 4>;      // 16 waves: 4 k-groups of 4
 using CfgL2 = TileCfg<128, 128, 32, 2, 2, 2>;    // 8 waves: 2 k-groups of 4
+using CfgL24 = TileCfg<128, 128, 32, 2, 4, 1, 4>;   // 8 waves, 64 x 32 per wave, 2 per CU
+using CfgL42 = TileCfg<128, 128, 32, 4, 2, 1, 4>;   // 8 waves, 32 x 64 per wave, 2 per CU
+using CfgW = TileCfg<256, 128, 32, 4, 2>;        // 8 waves, 64 x 64 per wave
+using CfgT = TileCfg<128, 256, 32, 2, 4>;        // 8 waves, 64 x 64 per wave
 
 struct ConfigInfo {
     const char *name;
@@ -968,6 +993,10 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_64x64x32_w2x2_kg2", CfgS2::BM, CfgS2::BN, CfgS2::NT},
     {"mfma32_64x64x32_w2x2_kg4", CfgS4::BM, CfgS4::BN, CfgS4::NT},
     {"mfma32_128x128x32_w2x2_kg2", CfgL2::BM, CfgL2::BN, CfgL2::NT},
+    {"mfma32_128x128x32_w2x4", CfgL24::BM, CfgL24::BN, CfgL24::NT},
+    {"mfma32_128x128x32_w4x2", CfgL42::BM, CfgL42::BN, CfgL42::NT},
+    {"mfma32_256x128x32_w4x2", CfgW::BM, CfgW::BN, CfgW::NT},
+    {"mfma32_128x256x32_w2x4", CfgT::BM, CfgT::BN, CfgT::NT},
 };
 constexpr int kSkinnyConfig = 2;
 constexpr int kBandConfig = 3;
@@ -1007,23 +1036,31 @@ double cu_balance(long long tiles) {
 
 // Shape class -> configuration, from per-configuration timings of the square
 // sweep, the layer shapes and the ragged shape on MI355X:
-//   M <= 32                      skinny band kernel (HBM-bound);
-//   >= 256 tiles of 128 x 128    128 x 128, unless 64 x 64 tiles spread more
-//                                evenly over the CUs by more than the 64 x 64
-//                                kernel's lower per-tile efficiency (0.87);
-//   192..255 such tiles          128 x 128 with two k-groups (8 waves);
-//   else, by 64 x 64 tiles:      >= 512 plain, > 256 two k-groups, else four.
+//   M <= 32             skinny band kernel (HBM-bound);
+//   >= 256 tiles of 128 x 128: the best of 256 x 128 (or 128 x 256 when
+//                       N > M; one workgroup per CU), 128 x 128 with 8 waves
+//                       and 64 x 64, each scored by how evenly its tiles spread
+//                       over the CUs times its efficiency on a large evenly
+//                       spread product (1.03 : 1 : 0.87);
+//   192..255 such tiles 128 x 128 with 8 waves;
+//   else, by 64 x 64 tiles: >= 512 plain, > 256 two k-groups, else four.
 int select_config(char transA, char transB, int M, int N, int K) {
     (void)transA;
     (void)transB;
     (void)K;
     if (M <= kSkinnyMaxM) return kBandConfig;
-    const long long tiles_l = (long long)((M + CfgL::BM - 1) / CfgL::BM) * ((N + CfgL::BN - 1) / CfgL::BN);
-    const long long tiles_s = (long long)((M + CfgS::BM - 1) / CfgS::BM) * ((N + CfgS::BN - 1) / CfgS::BN);
-    if (tiles_l >= kNumCus) return 0.87 * cu_balance(tiles_s) > cu_balance(tiles_l) ? 1 : 0;
-    if (tiles_l >= 3 * kNumCus / 4) return 6;
-    if (tiles_s >= 2 * kNumCus) return 1;
-    if (tiles_s > kNumCus) return 4;
+    auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    const long long t128 = tiles(128, 128), t64 = tiles(64, 64);
+    if (t128 >= kNumCus) {
+        const bool tall = M >= N;
+        const long long tbig = tall ? tiles(256, 128) : tiles(128, 256);
+        const double s_big = 1.03 * cu_balance(tbig), s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
+        if (s_big >= s_128 && s_big >= s_64) return tall ? 9 : 10;
+        return s_128 >= s_64 ? 8 : 1;
+    }
+    if (t128 >= 3 * kNumCus / 4) return 8;
+    if (t64 >= 2 * kNumCus) return 1;
+    if (t64 > kNumCus) return 4;
     return 5;
 }
 
@@ -1218,7 +1255,11 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case kBandConfig: err = launch_band(ta, tb, g, stream); break;
         case 4: err = launch_cfg<CfgS2>(ta, tb, g, stream); break;
         case 5: err = launch_cfg<CfgS4>(ta, tb, g, stream); break;
-        default: err = launch_cfg<CfgL2>(ta, tb, g, stream); break;
+        case 6: err = launch_cfg<CfgL2>(ta, tb, g, stream); break;
+        case 7: err = launch_cfg<CfgL24>(ta, tb, g, stream); break;
+        case 8: err = launch_cfg<CfgL42>(ta, tb, g, stream); break;
+        case 9: err = launch_cfg<CfgW>(ta, tb, g, stream); break;
+        default: err = launch_cfg<CfgT>(ta, tb, g, stream); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }
