@@ -71,13 +71,21 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int vec_ab;   // A and B: 16-byte aligned base, lda and ldb multiples of 4
     int vec_c;    // C: 16-byte aligned base, ldc multiple of 4
+    // Split-K over workgroups (tile kernels): `splits` workgroups per tile,
+    // each taking `kt_per_split` consecutive k-tiles; with splits > 1 their
+    // partial tiles meet in `ws` and `counters` (one counter per tile).
+    int splits, kt_per_split;
+    float *ws;
+    int *counters;
 };
 
 // BM x BN x BK macro tile; WAVES_M x WAVES_N waves share each k-tile; KG such
 // groups of waves take alternate k-tiles (split-K inside the workgroup), each
 // with its own LDS buffers, and are summed at the end in group order.
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1, int EU_ = 0>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1, int EU_ = 0, bool SPLIT_ = false>
 struct TileCfg {
+    // SPLIT: the kernel carries the split-K-over-workgroups reduction.
+    static constexpr bool SPLIT = SPLIT_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KG = KG_;
     static constexpr int NTG = 64 * WAVES_M * WAVES_N;   // threads per k-group
@@ -199,12 +207,16 @@ __device__ __forceinline__ void store_run(float *p, const float (&out)[n], float
 // j-th workgroup of XCD x is given logical tile prefix(x) + j, so each XCD
 // walks one contiguous run of logical tiles. Logical tiles are ordered in
 // groups of kGroupM tile rows, column by column within a group.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn) {
+// With split-K, the S workgroups of a tile are adjacent in logical order (so
+// usually on one XCD): logical = tile * S + split.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int splits, int &tm, int &tn, int &split) {
     const int bid = blockIdx.x;
     const int total = gridDim.x;
     const int q = total / kXcds, rem = total % kXcds;
     const int x = bid % kXcds, j = bid / kXcds;
-    const int logical = x * q + (x < rem ? x : rem) + j;
+    const int logical_ws = x * q + (x < rem ? x : rem) + j;
+    const int logical = logical_ws / splits;
+    split = logical_ws % splits;
     const int per_group = kGroupM * tiles_n;
     const int group = logical / per_group;
     const int first_m = group * kGroupM;
@@ -349,8 +361,8 @@ void sgemm_mfma32(GemmArgs g) {
     float *const a_lds = lds + grp * GROUP_FLOATS;
     float *const b_lds = a_lds + 2 * A_FLOATS;
 
-    int tm, tn;
-    tile_coords(g.tiles_m, g.tiles_n, tm, tn);
+    int tm, tn, split;
+    tile_coords(g.tiles_m, g.tiles_n, CFG::SPLIT ? g.splits : 1, tm, tn, split);
     const int m0 = tm * BM, n0 = tn * BN;
     const int M = g.M, N = g.N, K = g.K;
     const bool vec = g.vec_ab != 0;
@@ -358,7 +370,11 @@ void sgemm_mfma32(GemmArgs g) {
     const bool wg_fast = (m0 + BM <= M) && (n0 + BN <= N) && vec;
     const int kfull = K / BK;
     const int ktiles = (K + BK - 1) / BK;
-    const int rounds = (ktiles + KG - 1) / KG;
+    // This workgroup's k-tiles: [kt_begin, kt_end).
+    const int kt_begin = CFG::SPLIT ? split * g.kt_per_split : 0;
+    const int kt_end = CFG::SPLIT ? min(ktiles, kt_begin + g.kt_per_split) : ktiles;
+    const int kfast_end = min(kfull, kt_end);
+    const int rounds = kt_end > kt_begin ? (kt_end - kt_begin + KG - 1) / KG : 0;
 
     // Base of the tile at k = 0 in each stored matrix, and the per-k-tile step.
     const float *a_ptr = TA ? g.A + m0 : g.A + (size_t)m0 * g.lda;
@@ -392,26 +408,27 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Group grp takes k-tiles grp, grp + KG, ... In round r its k-tile is
-    // t = r*KG + grp. Invariant at the top of round r: the group's LDS buffer
-    // r&1 holds k-tile t (when t < ktiles) and f0 holds its q-group 0.
+    // Group grp takes k-tiles kt_begin + grp, + KG, ... In round r its k-tile
+    // is t = kt_begin + r*KG + grp. Invariant at the top of round r: the
+    // group's LDS buffer r&1 holds k-tile t (when t < kt_end) and f0 holds
+    // its q-group 0.
     F f0, f1;
-    if (grp < ktiles) {
-        fetch_any(grp);
+    if (kt_begin + grp < kt_end) {
+        fetch_any(kt_begin + grp);
         ca.store(a_lds, gtid);
         cb.store(b_lds, gtid);
     }
     __syncthreads();
-    if (grp < ktiles) f0.template read<AS, BS>(a_lds, b_lds, 0, wm, wn, li, lh);
+    if (kt_begin + grp < kt_end) f0.template read<AS, BS>(a_lds, b_lds, 0, wm, wn, li, lh);
 
     for (int r = 0; r < rounds; ++r) {
-        const int t = r * KG + grp, tn_ = t + KG;
+        const int t = kt_begin + r * KG + grp, tn_ = t + KG;
         const int cur = r & 1, nxt = cur ^ 1;
         const float *as = a_lds + cur * A_FLOATS;
         const float *bs = b_lds + cur * B_FLOATS;
         float *as_n = a_lds + nxt * A_FLOATS;
         float *bs_n = b_lds + nxt * B_FLOATS;
-        if (wg_fast && tn_ < kfull) {
+        if (wg_fast && tn_ < kfast_end) {
             // Straight-line round: this and the next k-tile are complete and in range.
             fetch_fast(tn_);
 #pragma unroll
@@ -433,7 +450,7 @@ void sgemm_mfma32(GemmArgs g) {
             __syncthreads();
             f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
         } else {
-            const bool has_cur = t < ktiles, has_next = tn_ < ktiles;
+            const bool has_cur = t < kt_end, has_next = tn_ < kt_end;
             if (has_next) fetch_any(tn_);
             if (has_cur) {
 #pragma unroll
@@ -469,7 +486,9 @@ void sgemm_mfma32(GemmArgs g) {
                     for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
         }
         __syncthreads();
-        if (grp > 0) return;
+        // Without split-K no barrier follows, so the other groups are done.
+        if (!CFG::SPLIT && grp > 0) return;
+        if (grp == 0)
 #pragma unroll
         for (int g2 = 1; g2 < KG; ++g2) {
             const float *src = lds + ((g2 - 1) * WAVES + wave) * SLOT + lane;
@@ -481,6 +500,74 @@ void sgemm_mfma32(GemmArgs g) {
                     for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
         }
     }
+
+    if constexpr (CFG::SPLIT) if (g.splits > 1) {
+        // Split-K over workgroups: store this partial tile (group 0's
+        // accumulators, in register order) to the workspace with system-scope
+        // stores, count in, and let the workgroup that completes the count sum
+        // the partials in split order before the epilogue. Same protocol as the
+        // skinny band kernel; every wave of the workgroup reaches each barrier.
+        constexpr int REGS = FM * FN * 16;
+        constexpr size_t PART = (size_t)BM * BN;
+        __shared__ int is_last;
+        const int S = g.splits;
+        const size_t tile_id = (size_t)tm * g.tiles_n + tn;
+        float *mine = g.ws + (tile_id * S + split) * PART + (size_t)wave * REGS * 64 + lane;
+        if (grp == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        __hip_atomic_store(mine + ((i * FN + j) * 16 + r) * 64, acc[i][j][r], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            is_last = __hip_atomic_fetch_add(&g.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                      S - 1;
+        __syncthreads();
+        if (!is_last) return;
+        const float *base = g.ws + tile_id * S * PART + (size_t)wave * REGS * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        // SB splits' loads in flight at a time (about 64 registers); the sum
+        // runs in split order.
+        constexpr int SB = REGS >= 64 ? 1 : 64 / REGS;
+        for (int sp0 = 0; sp0 < S; sp0 += SB) {
+            float v[SB][FM][FN][16];
+#pragma unroll
+            for (int u = 0; u < SB; ++u)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            v[u][i][j][r] = (grp == 0 && sp0 + u < S)
+                                                ? __hip_atomic_load(base + (size_t)(sp0 + u) * PART +
+                                                                        ((i * FN + j) * 16 + r) * 64,
+                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                                                : 0.0f;
+#pragma unroll
+            for (int u = 0; u < SB; ++u)
+                if (sp0 + u < S)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) acc[i][j][r] += v[u][i][j][r];
+        }
+        if (tid == 0) __hip_atomic_store(&g.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    if (grp > 0) return;
 
     // Epilogue. Accumulator element r of block (i, j) in lane (li, lh) is
     // block row 8*(r/4) + 4*lh + r%4, block column li.
@@ -979,6 +1066,10 @@ using CfgL24 = TileCfg<128, 128, 32, 2, 4, 1, 4>;   // 8 waves, 64 x 32 per wave
 using CfgL42 = TileCfg<128, 128, 32, 4, 2, 1, 4>;   // 8 waves, 32 x 64 per wave, 2 per CU
 using CfgW = TileCfg<256, 128, 32, 4, 2>;        // 8 waves, 64 x 64 per wave
 using CfgT = TileCfg<128, 256, 32, 2, 4>;        // 8 waves, 64 x 64 per wave
+// Split-K over workgroups (for grids with fewer tiles than CU slots).
+using CfgL42K = TileCfg<128, 128, 32, 4, 2, 1, 4, true>;
+using CfgSK = TileCfg<64, 64, 32, 2, 2, 1, 0, true>;
+using CfgLK = TileCfg<128, 128, 32, 2, 2, 1, 0, true>;
 
 struct ConfigInfo {
     const char *name;
@@ -997,6 +1088,9 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_128x128x32_w4x2", CfgL42::BM, CfgL42::BN, CfgL42::NT},
     {"mfma32_256x128x32_w4x2", CfgW::BM, CfgW::BN, CfgW::NT},
     {"mfma32_128x256x32_w2x4", CfgT::BM, CfgT::BN, CfgT::NT},
+    {"mfma32_128x128x32_w4x2_splitk", CfgL42K::BM, CfgL42K::BN, CfgL42K::NT},
+    {"mfma32_64x64x32_w2x2_splitk", CfgSK::BM, CfgSK::BN, CfgSK::NT},
+    {"mfma32_128x128x32_w2x2_splitk", CfgLK::BM, CfgLK::BN, CfgLK::NT},
 };
 constexpr int kSkinnyConfig = 2;
 constexpr int kBandConfig = 3;
@@ -1043,7 +1137,10 @@ double cu_balance(long long tiles) {
 //                       over the CUs times its efficiency on a large evenly
 //                       spread product (1.03 : 1 : 0.87);
 //   192..255 such tiles 128 x 128 with 8 waves;
-//   else, by 64 x 64 tiles: >= 512 plain, > 256 two k-groups, else four.
+//   else, by 64 x 64 tiles: >= 512 plain; 257..511 two k-groups, or split-K
+//                       over workgroups when those would fill under 70% of
+//                       the CU slots; <= 96 split-K over workgroups; else
+//                       four k-groups.
 int select_config(char transA, char transB, int M, int N, int K) {
     (void)transA;
     (void)transB;
@@ -1060,7 +1157,12 @@ int select_config(char transA, char transB, int M, int N, int K) {
     }
     if (t128 >= 3 * kNumCus / 4) return 8;
     if (t64 >= 2 * kNumCus) return 1;
-    if (t64 > kNumCus) return 4;
+    // 257..511 tiles of 64 x 64: two k-groups unless their workgroups would
+    // leave the CU slots badly filled; then split-K over workgroups, whose
+    // smaller workgroups spread more evenly.
+    if (t64 > kNumCus) return (double)t64 / (2 * kNumCus) >= 0.7 ? 4 : 12;
+    // Up to 96 tiles of 64 x 64 (n <= ~600): split-K over workgroups.
+    if (t64 <= 96) return 12;
     return 5;
 }
 
@@ -1068,7 +1170,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 template <class CFG, bool TA, bool TB>
 hipError_t launch_t(const GemmArgs &g, hipStream_t stream) {
-    dim3 grid((unsigned)(g.tiles_m * g.tiles_n));
+    dim3 grid((unsigned)(g.tiles_m * g.tiles_n * g.splits));
     dim3 block(CFG::NT);
     hipLaunchKernelGGL((sgemm_mfma32<CFG, TA, TB>), grid, block, 0, stream, g);
     return hipGetLastError();
@@ -1077,7 +1179,7 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t stream) {
 // Workspace for the split-K reduction, one per (device, stream) so that calls
 // on different streams never share partials or counters. Allocated on the
 // first call that needs it and kept until the process ends.
-constexpr size_t kWsFloats = size_t(4) << 20;   // 16 MiB of partial blocks
+constexpr size_t kWsFloats = size_t(8) << 20;   // 32 MiB of partial blocks
 constexpr int kWsCounters = 1 << 16;
 
 struct Workspace {
@@ -1200,9 +1302,38 @@ hipError_t launch_skinny(bool ta, bool tb, const GemmArgs &g, hipStream_t stream
 }
 
 template <class CFG>
-hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream) {
+hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int split_slots = 0) {
     g.tiles_m = (g.M + CFG::BM - 1) / CFG::BM;
     g.tiles_n = (g.N + CFG::BN - 1) / CFG::BN;
+    const int ktiles = (g.K + CFG::BK - 1) / CFG::BK;
+    g.splits = 1;
+    g.kt_per_split = ktiles;
+    g.ws = nullptr;
+    g.counters = nullptr;
+    if (CFG::SPLIT && split_slots > 0) {
+        // Split-K over workgroups: about one workgroup per CU slot, at least
+        // four k-tiles per split, within the workspace.
+        const long long tiles = (long long)g.tiles_m * g.tiles_n;
+        long long S = ((long long)kNumCus * split_slots + tiles - 1) / tiles;
+        if (S > ktiles / 4) S = ktiles / 4;
+        if (S > kMaxSplits) S = kMaxSplits;
+        if (S < 1) S = 1;
+        while (S > 1 && tiles * S * CFG::BM * CFG::BN > (long long)kWsFloats) --S;
+        if (tiles > kWsCounters) S = 1;
+        if (S > 1) {
+            const Workspace *w = get_workspace(stream);
+            if (w == nullptr) {
+                S = 1;
+            } else {
+                g.ws = w->partials;
+                g.counters = w->counters;
+                g.kt_per_split = (int)((ktiles + S - 1) / S);
+                S = (ktiles + g.kt_per_split - 1) / g.kt_per_split;
+            }
+        }
+        g.splits = (int)S;
+        if (g.splits == 1) g.kt_per_split = ktiles;
+    }
     if (!ta && !tb) return launch_t<CFG, false, false>(g, stream);
     if (!ta && tb) return launch_t<CFG, false, true>(g, stream);
     if (ta && !tb) return launch_t<CFG, true, false>(g, stream);
@@ -1241,6 +1372,10 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     g.ldc = ldc;
     g.alpha = alpha;
     g.beta = beta;
+    g.splits = 1;
+    g.kt_per_split = 0;
+    g.ws = nullptr;
+    g.counters = nullptr;
     g.vec_ab = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;
     g.vec_c = aligned16(C) && ldc % 4 == 0;
     const bool ta = op_t(transA), tb = op_t(transB);
@@ -1259,7 +1394,10 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case 7: err = launch_cfg<CfgL24>(ta, tb, g, stream); break;
         case 8: err = launch_cfg<CfgL42>(ta, tb, g, stream); break;
         case 9: err = launch_cfg<CfgW>(ta, tb, g, stream); break;
-        default: err = launch_cfg<CfgT>(ta, tb, g, stream); break;
+        case 10: err = launch_cfg<CfgT>(ta, tb, g, stream); break;
+        case 11: err = launch_cfg<CfgL42K>(ta, tb, g, stream, 1); break;
+        case 12: err = launch_cfg<CfgSK>(ta, tb, g, stream, 2); break;
+        default: err = launch_cfg<CfgLK>(ta, tb, g, stream, 1); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }

@@ -114,7 +114,10 @@ def test_shape_class_selection():
     assert sel("T", "T", 2048, 4096, 1024) == "mfma32_128x256x32_w2x4"
     # 1024^2 output: 64 tiles of 128 x 128 only, so smaller tiles with four k-groups.
     assert sel("N", "N", 1024, 1024, 1024) == "mfma32_64x64x32_w2x2_kg4"
-    assert sel("N", "N", 1000, 1300, 700) == "mfma32_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 1000, 1300, 700) == "mfma32_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 1280, 1280, 1280) == "mfma32_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 512, 512, 512) == "mfma32_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 768, 768, 768) == "mfma32_64x64x32_w2x2_kg4"
     assert sel("N", "N", 1792, 1792, 1792) == "mfma32_128x128x32_w4x2"
     assert sel("N", "N", 1536, 1536, 1536) == "mfma32_64x64x32_w2x2"
     # Square sizes: whichever tile spreads most evenly over the 256 CUs.
