@@ -1066,6 +1066,7 @@ using CfgL24 = TileCfg<128, 128, 32, 2, 4, 1, 4>;   // 8 waves, 64 x 32 per wave
 using CfgL42 = TileCfg<128, 128, 32, 4, 2, 1, 4>;   // 8 waves, 32 x 64 per wave, 2 per CU
 using CfgW = TileCfg<256, 128, 32, 4, 2>;        // 8 waves, 64 x 64 per wave
 using CfgT = TileCfg<128, 256, 32, 2, 4>;        // 8 waves, 64 x 64 per wave
+using CfgT16 = TileCfg<128, 256, 16, 2, 2>;      // 4 waves, 64 x 128 per wave, 2 per CU
 // Split-K over workgroups (for grids with fewer tiles than CU slots).
 using CfgL42K = TileCfg<128, 128, 32, 4, 2, 1, 4, true>;
 using CfgSK = TileCfg<64, 64, 32, 2, 2, 1, 0, true>;
@@ -1091,6 +1092,7 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_128x128x32_w4x2_splitk", CfgL42K::BM, CfgL42K::BN, CfgL42K::NT},
     {"mfma32_64x64x32_w2x2_splitk", CfgSK::BM, CfgSK::BN, CfgSK::NT},
     {"mfma32_128x128x32_w2x2_splitk", CfgLK::BM, CfgLK::BN, CfgLK::NT},
+    {"mfma32_128x256x16_w2x2", CfgT16::BM, CfgT16::BN, CfgT16::NT},
 };
 constexpr int kSkinnyConfig = 2;
 constexpr int kBandConfig = 3;
@@ -1121,21 +1123,28 @@ int check_args(char transA, char transB, int M, int N, int K, float alpha, const
     return MISGEMM_SUCCESS;
 }
 
-// Fraction of the busiest CU's tile slots that hold work when `tiles`
-// workgroups are spread over the CUs: 1 when every CU gets the same count.
-double cu_balance(long long tiles) {
-    const long long per_cu = (tiles + kNumCus - 1) / kNumCus;
-    return (double)tiles / (double)(per_cu * kNumCus);
+// Fraction of the busiest CU's workgroup slots that hold work when `tiles`
+// workgroups are spread over the CUs, `slots` at a time per CU: 1 when every
+// CU gets the same count.
+double cu_balance(long long tiles, int slots = 1) {
+    const long long cap = (long long)kNumCus * slots;
+    const long long rounds = (tiles + cap - 1) / cap;
+    return (double)tiles / (double)(rounds * cap);
 }
 
 // Shape class -> configuration, from per-configuration timings of the square
-// sweep, the layer shapes and the ragged shape on MI355X:
+// sweep, the layer shapes and the ragged shape on MI355X (bench.py
+// --sweep-configs):
 //   M <= 32             skinny band kernel (HBM-bound);
-//   >= 256 tiles of 128 x 128: the best of 256 x 128 (or 128 x 256 when
-//                       N > M; one workgroup per CU), 128 x 128 with 8 waves
-//                       and 64 x 64, each scored by how evenly its tiles spread
-//                       over the CUs times its efficiency on a large evenly
-//                       spread product (1.03 : 1 : 0.87);
+//   >= 256 tiles of 128 x 128: the best-scoring of
+//                       128 x 256 with 4 waves (two workgroups per CU; B
+//                         not transposed)                    1.038 x balance over 2 slots per CU
+//                       256 x 128 / 128 x 256 with 8 waves (one per CU; B
+//                         not transposed)                    1.024 x balance
+//                       128 x 128 with 8 waves                   1 x balance
+//                       64 x 64                               0.87 x balance
+//                       (the factors are their relative speeds on a large,
+//                       evenly spread product);
 //   192..255 such tiles 128 x 128 with 8 waves;
 //   else, by 64 x 64 tiles: >= 512 plain; 257..511 two k-groups, or split-K
 //                       over workgroups when those would fill under 70% of
@@ -1143,17 +1152,20 @@ double cu_balance(long long tiles) {
 //                       four k-groups.
 int select_config(char transA, char transB, int M, int N, int K) {
     (void)transA;
-    (void)transB;
     (void)K;
     if (M <= kSkinnyMaxM) return kBandConfig;
     auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const long long t128 = tiles(128, 128), t64 = tiles(64, 64);
     if (t128 >= kNumCus) {
+        const bool tb = op_t(transB);
         const bool tall = M >= N;
-        const long long tbig = tall ? tiles(256, 128) : tiles(128, 256);
-        const double s_big = 1.03 * cu_balance(tbig), s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
-        if (s_big >= s_128 && s_big >= s_64) return tall ? 9 : 10;
-        return s_128 >= s_64 ? 8 : 1;
+        const double s_b4 = tb ? -1.0 : 1.038 * cu_balance(tiles(128, 256), 2);
+        const double s_b8 = tb ? -1.0 : 1.024 * cu_balance(tall ? tiles(256, 128) : tiles(128, 256));
+        const double s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
+        const double best = fmax(fmax(s_b4, s_b8), fmax(s_128, s_64));
+        if (best == s_b4) return 14;
+        if (best == s_b8) return tall ? 9 : 10;
+        return best == s_128 ? 8 : 1;
     }
     if (t128 >= 3 * kNumCus / 4) return 8;
     if (t64 >= 2 * kNumCus) return 1;
@@ -1397,7 +1409,8 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case 10: err = launch_cfg<CfgT>(ta, tb, g, stream); break;
         case 11: err = launch_cfg<CfgL42K>(ta, tb, g, stream, 1); break;
         case 12: err = launch_cfg<CfgSK>(ta, tb, g, stream, 2); break;
-        default: err = launch_cfg<CfgLK>(ta, tb, g, stream, 1); break;
+        case 13: err = launch_cfg<CfgLK>(ta, tb, g, stream, 1); break;
+        default: err = launch_cfg<CfgT16>(ta, tb, g, stream); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }
