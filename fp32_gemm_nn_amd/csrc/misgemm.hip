@@ -408,11 +408,11 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    F f0, f1;
     // Group grp takes k-tiles kt_begin + grp, + KG, ... In round r its k-tile
     // is t = kt_begin + r*KG + grp. Invariant at the top of round r: the
     // group's LDS buffer r&1 holds k-tile t (when t < kt_end) and f0 holds
     // its q-group 0.
-    F f0, f1;
     if (kt_begin + grp < kt_end) {
         fetch_any(kt_begin + grp);
         ca.store(a_lds, gtid);
@@ -421,16 +421,18 @@ void sgemm_mfma32(GemmArgs g) {
     __syncthreads();
     if (kt_begin + grp < kt_end) f0.template read<AS, BS>(a_lds, b_lds, 0, wm, wn, li, lh);
 
-    for (int r = 0; r < rounds; ++r) {
-        const int t = kt_begin + r * KG + grp, tn_ = t + KG;
-        const int cur = r & 1, nxt = cur ^ 1;
-        const float *as = a_lds + cur * A_FLOATS;
-        const float *bs = b_lds + cur * B_FLOATS;
-        float *as_n = a_lds + nxt * A_FLOATS;
-        float *bs_n = b_lds + nxt * B_FLOATS;
-        if (wg_fast && tn_ < kfast_end) {
-            // Straight-line round: this and the next k-tile are complete and in range.
-            fetch_fast(tn_);
+    // Straight-line rounds (this and the next k-tile complete and in
+    // range) first, then the guarded ones, as two loops; the condition
+    // holds for a prefix of the rounds, and both kinds end on one barrier.
+    int r = 0;
+    if (wg_fast) {
+        for (; kt_begin + (r + 1) * KG + grp < kfast_end; ++r) {
+            const int cur = r & 1, nxt = cur ^ 1;
+            const float *as = a_lds + cur * A_FLOATS;
+            const float *bs = b_lds + cur * B_FLOATS;
+            float *as_n = a_lds + nxt * A_FLOATS;
+            float *bs_n = b_lds + nxt * B_FLOATS;
+            fetch_fast(kt_begin + (r + 1) * KG + grp);
 #pragma unroll
             for (int q = 0; q < Q; q += 2) {
                 f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
@@ -449,25 +451,32 @@ void sgemm_mfma32(GemmArgs g) {
                                (TA ? 4 : FM) + (TB ? FN : 4), ACopy::PER_THREAD + BCopy::PER_THREAD>();
             __syncthreads();
             f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
-        } else {
-            const bool has_cur = t < kt_end, has_next = tn_ < kt_end;
-            if (has_next) fetch_any(tn_);
-            if (has_cur) {
-#pragma unroll
-                for (int q = 0; q < Q; q += 2) {
-                    f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
-                    f0.mma(acc);
-                    if (q + 2 < Q) f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
-                    f1.mma(acc);
-                }
-            }
-            if (has_next) {
-                ca.store(as_n, gtid);
-                cb.store(bs_n, gtid);
-            }
-            __syncthreads();
-            if (has_next) f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
         }
+    }
+    for (; r < rounds; ++r) {
+        const int t = kt_begin + r * KG + grp, tn_ = t + KG;
+        const int cur = r & 1, nxt = cur ^ 1;
+        const float *as = a_lds + cur * A_FLOATS;
+        const float *bs = b_lds + cur * B_FLOATS;
+        float *as_n = a_lds + nxt * A_FLOATS;
+        float *bs_n = b_lds + nxt * B_FLOATS;
+        const bool has_cur = t < kt_end, has_next = tn_ < kt_end;
+        if (has_next) fetch_any(tn_);
+        if (has_cur) {
+#pragma unroll
+            for (int q = 0; q < Q; q += 2) {
+                f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
+                f0.mma(acc);
+                if (q + 2 < Q) f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
+                f1.mma(acc);
+            }
+        }
+        if (has_next) {
+            ca.store(as_n, gtid);
+            cb.store(bs_n, gtid);
+        }
+        __syncthreads();
+        if (has_next) f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
     }
 
     if constexpr (KG > 1) {
@@ -1067,6 +1076,7 @@ using CfgL42 = TileCfg<128, 128, 32, 4, 2, 1, 4>;   // 8 waves, 32 x 64 per wave
 using CfgW = TileCfg<256, 128, 32, 4, 2>;        // 8 waves, 64 x 64 per wave
 using CfgT = TileCfg<128, 256, 32, 2, 4>;        // 8 waves, 64 x 64 per wave
 using CfgT16 = TileCfg<128, 256, 16, 2, 2>;      // 4 waves, 64 x 128 per wave, 2 per CU
+using CfgQ32 = TileCfg<256, 256, 32, 4, 2>;      // 8 waves, 64 x 128 per wave, 1 per CU
 // Split-K over workgroups (for grids with fewer tiles than CU slots).
 using CfgL42K = TileCfg<128, 128, 32, 4, 2, 1, 4, true>;
 using CfgSK = TileCfg<64, 64, 32, 2, 2, 1, 0, true>;
@@ -1093,6 +1103,7 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_64x64x32_w2x2_splitk", CfgSK::BM, CfgSK::BN, CfgSK::NT},
     {"mfma32_128x128x32_w2x2_splitk", CfgLK::BM, CfgLK::BN, CfgLK::NT},
     {"mfma32_128x256x16_w2x2", CfgT16::BM, CfgT16::BN, CfgT16::NT},
+    {"mfma32_256x256x32_w4x2", CfgQ32::BM, CfgQ32::BN, CfgQ32::NT},
 };
 constexpr int kSkinnyConfig = 2;
 constexpr int kBandConfig = 3;
@@ -1137,6 +1148,8 @@ double cu_balance(long long tiles, int slots = 1) {
 // --sweep-configs):
 //   M <= 32             skinny band kernel (HBM-bound);
 //   >= 256 tiles of 128 x 128: the best-scoring of
+//                       256 x 256 with 8 waves (one per CU; B not
+//                         transposed)                        1.044 x balance
 //                       128 x 256 with 4 waves (two workgroups per CU; B
 //                         not transposed)                    1.038 x balance over 2 slots per CU
 //                       256 x 128 / 128 x 256 with 8 waves (one per CU; B
@@ -1159,10 +1172,12 @@ int select_config(char transA, char transB, int M, int N, int K) {
     if (t128 >= kNumCus) {
         const bool tb = op_t(transB);
         const bool tall = M >= N;
+        const double s_q = tb ? -1.0 : 1.044 * cu_balance(tiles(256, 256));
         const double s_b4 = tb ? -1.0 : 1.038 * cu_balance(tiles(128, 256), 2);
         const double s_b8 = tb ? -1.0 : 1.024 * cu_balance(tall ? tiles(256, 128) : tiles(128, 256));
         const double s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
-        const double best = fmax(fmax(s_b4, s_b8), fmax(s_128, s_64));
+        const double best = fmax(fmax(s_q, fmax(s_b4, s_b8)), fmax(s_128, s_64));
+        if (best == s_q) return 15;
         if (best == s_b4) return 14;
         if (best == s_b8) return tall ? 9 : 10;
         return best == s_128 ? 8 : 1;
@@ -1410,7 +1425,8 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case 11: err = launch_cfg<CfgL42K>(ta, tb, g, stream, 1); break;
         case 12: err = launch_cfg<CfgSK>(ta, tb, g, stream, 2); break;
         case 13: err = launch_cfg<CfgLK>(ta, tb, g, stream, 1); break;
-        default: err = launch_cfg<CfgT16>(ta, tb, g, stream); break;
+        case 14: err = launch_cfg<CfgT16>(ta, tb, g, stream); break;
+        default: err = launch_cfg<CfgQ32>(ta, tb, g, stream); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }

@@ -109,8 +109,11 @@ def test_with_config_rejects_unknown_id():
 def test_shape_class_selection():
     names = mg.config_names()
     sel = lambda *s: names[mg.mi_sgemm_select_config(*s)]
-    # 4096^2 output: 512 tiles of 128 x 256, two per CU.
-    assert sel("N", "N", 4096, 4096, 4096) == "mfma32_128x256x16_w2x2"
+    # 4096^2 output: 256 tiles of 256 x 256, one per CU.
+    assert sel("N", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
+    assert sel("T", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
+    # B transposed: no big tiles; 128 x 128 with 8 waves.
+    assert sel("N", "T", 4096, 4096, 4096) == "mfma32_128x128x32_w4x2"
     # 2048 x 4096: 256 such tiles only (one per CU): the 8-wave big tile,
     # unless B is transposed.
     assert sel("N", "N", 2048, 4096, 1024) == "mfma32_128x256x32_w2x4"
@@ -128,7 +131,8 @@ def test_shape_class_selection():
     # Square sizes: whichever tile spreads most evenly over the 256 CUs.
     for n, want in [(2048, "128x128x32_w4x2"), (2304, "64x64x32_w2x2"), (2560, "256x128x32_w4x2"),
                     (2816, "256x128x32_w4x2"), (3072, "64x64x32_w2x2"), (3328, "128x128x32_w4x2"),
-                    (3584, "64x64x32_w2x2"), (3840, "128x256x16_w2x2"), (4096, "128x256x16_w2x2")]:
+                    (3584, "64x64x32_w2x2"), (3840, "256x256x32_w4x2"), (4096, "256x256x32_w4x2"),
+                    (8192, "256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == "mfma32_" + want, n
     # M <= 32: the skinny, bandwidth-bound kernel.
     assert "skinny" in sel("N", "N", 16, 4096, 4096)
