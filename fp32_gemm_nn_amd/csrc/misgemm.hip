@@ -45,6 +45,7 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -82,10 +83,14 @@ struct GemmArgs {
 // BM x BN x BK macro tile; WAVES_M x WAVES_N waves share each k-tile; KG such
 // groups of waves take alternate k-tiles (split-K inside the workgroup), each
 // with its own LDS buffers, and are summed at the end in group order.
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1, int EU_ = 0, bool SPLIT_ = false>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1, int EU_ = 0, bool SPLIT_ = false,
+          bool STREAMK_ = false>
 struct TileCfg {
     // SPLIT: the kernel carries the split-K-over-workgroups reduction.
     static constexpr bool SPLIT = SPLIT_;
+    // STREAMK: one workgroup per CU walks an equal share of all (tile,
+    // k-tile) iterations; tiles cut between workgroups use the same reduction.
+    static constexpr bool STREAMK = STREAMK_;
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, KG = KG_;
     static constexpr int NTG = 64 * WAVES_M * WAVES_N;   // threads per k-group
@@ -209,14 +214,15 @@ __device__ __forceinline__ void store_run(float *p, const float (&out)[n], float
 // groups of kGroupM tile rows, column by column within a group.
 // With split-K, the S workgroups of a tile are adjacent in logical order (so
 // usually on one XCD): logical = tile * S + split.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int splits, int &tm, int &tn, int &split) {
+__device__ __forceinline__ int xcd_logical() {
     const int bid = blockIdx.x;
     const int total = gridDim.x;
     const int q = total / kXcds, rem = total % kXcds;
     const int x = bid % kXcds, j = bid / kXcds;
-    const int logical_ws = x * q + (x < rem ? x : rem) + j;
-    const int logical = logical_ws / splits;
-    split = logical_ws % splits;
+    return x * q + (x < rem ? x : rem) + j;
+}
+
+__device__ __forceinline__ void tile_of(int logical, int tiles_m, int tiles_n, int &tm, int &tn) {
     const int per_group = kGroupM * tiles_n;
     const int group = logical / per_group;
     const int first_m = group * kGroupM;
@@ -225,6 +231,21 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int splits
     tm = first_m + in_g % gsz;
     tn = in_g / gsz;
 }
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int splits, int &tm, int &tn, int &split) {
+    const int logical_ws = xcd_logical();
+    split = logical_ws % splits;
+    tile_of(logical_ws / splits, tiles_m, tiles_n, tm, tn);
+}
+
+// One tile's share of the k-range in a split product: segment seg of nseg (in
+// k order), the tile's counter, and where segment j keeps its partial block:
+// workspace slot s0 for j = 0, sbase + j*sstep after that.
+struct SegInfo {
+    int nseg, seg, counter;
+    int s0, sbase, sstep;
+    __device__ __forceinline__ int slot(int j) const { return j == 0 ? s0 : sbase + j * sstep; }
+};
 
 // MFMA operands of one q-group (four consecutive k-steps of a k-tile) for one
 // wave: a[blk][e] and b[blk][e] feed step e of the 32x32x2 MFMA for block blk.
@@ -352,265 +373,325 @@ void sgemm_mfma32(GemmArgs g) {
 
     __shared__ __attribute__((aligned(16))) float lds[KG * GROUP_FLOATS];
 
-    const int tid = threadIdx.x;
-    const int grp = tid / NTG, gtid = tid % NTG;     // k-group and thread within it
-    const int lane = gtid & 63, wave = gtid >> 6;
-    const int li = lane & 31, lh = lane >> 5;
-    const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
-    // This group's buffer i of A at a_lds + i*A_FLOATS, of B at b_lds + i*B_FLOATS.
-    float *const a_lds = lds + grp * GROUP_FLOATS;
-    float *const b_lds = a_lds + 2 * A_FLOATS;
+    __shared__ int is_last;
+    const int ktiles = (g.K + BK - 1) / BK;
 
-    int tm, tn, split;
-    tile_coords(g.tiles_m, g.tiles_n, CFG::SPLIT ? g.splits : 1, tm, tn, split);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int M = g.M, N = g.N, K = g.K;
-    const bool vec = g.vec_ab != 0;
-    // Interior workgroup: every complete k-tile can be fetched unguarded.
-    const bool wg_fast = (m0 + BM <= M) && (n0 + BN <= N) && vec;
-    const int kfull = K / BK;
-    const int ktiles = (K + BK - 1) / BK;
-    // This workgroup's k-tiles: [kt_begin, kt_end).
-    const int kt_begin = CFG::SPLIT ? split * g.kt_per_split : 0;
-    const int kt_end = CFG::SPLIT ? min(ktiles, kt_begin + g.kt_per_split) : ktiles;
-    const int kfast_end = min(kfull, kt_end);
-    const int rounds = kt_end > kt_begin ? (kt_end - kt_begin + KG - 1) / KG : 0;
+    // Tile (tm, tn), k-tiles [kt_begin, kt_end), into C; or, when sg.nseg > 1,
+    // into a partial block that the last of the tile's segments to finish
+    // adds up in segment order before the epilogue.
+    auto run_tile = [&](const int tm, const int tn, const int kt_begin, const int kt_end, const SegInfo &sg) {
+        // Thread coordinates. A stream-K workgroup walks several tiles: the
+        // empty asm makes the thread id opaque per tile, so the addresses
+        // derived from it are recomputed per tile instead of being hoisted
+        // out of the tile loop and held live across every k-loop.
+        int tid = threadIdx.x;
+        if constexpr (CFG::STREAMK) asm volatile("" : "+v"(tid));
+        const int grp = KG == 1 ? 0 : tid / NTG;    // k-group
+        const int gtid = KG == 1 ? tid : tid % NTG;  // thread within it
+        const int lane = gtid & 63, wave = gtid >> 6;
+        const int li = lane & 31, lh = lane >> 5;
+        const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
+        // This group's buffer i of A at a_lds + i*A_FLOATS, of B at b_lds + i*B_FLOATS.
+        float *const a_lds = lds + grp * GROUP_FLOATS;
+        float *const b_lds = a_lds + 2 * A_FLOATS;
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int M = g.M, N = g.N, K = g.K;
+        const bool vec = g.vec_ab != 0;
+        // Interior workgroup: every complete k-tile can be fetched unguarded.
+        const bool wg_fast = (m0 + BM <= M) && (n0 + BN <= N) && vec;
+        const int kfull = K / BK;
+        const int kfast_end = min(kfull, kt_end);
+        const int rounds = kt_end > kt_begin ? (kt_end - kt_begin + KG - 1) / KG : 0;
 
-    // Base of the tile at k = 0 in each stored matrix, and the per-k-tile step.
-    const float *a_ptr = TA ? g.A + m0 : g.A + (size_t)m0 * g.lda;
-    const float *b_ptr = TB ? g.B + (size_t)n0 * g.ldb : g.B + n0;
-    const size_t a_step = TA ? (size_t)BK * g.lda : (size_t)BK;
-    const size_t b_step = TB ? (size_t)BK : (size_t)BK * g.ldb;
-    const int a_rows = TA ? K : M - m0, a_cols = TA ? M - m0 : K;
-    const int b_rows = TB ? N - n0 : K, b_cols = TB ? K : N - n0;
+        // Base of the tile at k = 0 in each stored matrix, and the per-k-tile step.
+        const float *a_ptr = TA ? g.A + m0 : g.A + (size_t)m0 * g.lda;
+        const float *b_ptr = TB ? g.B + (size_t)n0 * g.ldb : g.B + n0;
+        const size_t a_step = TA ? (size_t)BK * g.lda : (size_t)BK;
+        const size_t b_step = TB ? (size_t)BK : (size_t)BK * g.ldb;
+        const int a_rows = TA ? K : M - m0, a_cols = TA ? M - m0 : K;
+        const int b_rows = TB ? N - n0 : K, b_cols = TB ? K : N - n0;
 
-    ACopy ca;
-    BCopy cb;
-    auto fetch_fast = [&](int kt) {
-        ca.load(a_ptr + kt * a_step, g.lda, 0, 0, false, true, gtid);
-        cb.load(b_ptr + kt * b_step, g.ldb, 0, 0, false, true, gtid);
-    };
-    auto fetch_any = [&](int kt) {
-        const int k0 = kt * BK;
-        const bool guard = !(wg_fast && kt < kfull);
-        // Rows/cols left counted from this k-tile's origin.
-        ca.load(a_ptr + kt * a_step, g.lda, TA ? a_rows - k0 : a_rows, TA ? a_cols : a_cols - k0,
-                guard, vec, gtid);
-        cb.load(b_ptr + kt * b_step, g.ldb, TB ? b_rows : b_rows - k0, TB ? b_cols - k0 : b_cols,
-                guard, vec, gtid);
-    };
+        ACopy ca;
+        BCopy cb;
+        auto fetch_fast = [&](int kt) {
+            ca.load(a_ptr + kt * a_step, g.lda, 0, 0, false, true, gtid);
+            cb.load(b_ptr + kt * b_step, g.ldb, 0, 0, false, true, gtid);
+        };
+        auto fetch_any = [&](int kt) {
+            const int k0 = kt * BK;
+            const bool guard = !(wg_fast && kt < kfull);
+            // Rows/cols left counted from this k-tile's origin.
+            ca.load(a_ptr + kt * a_step, g.lda, TA ? a_rows - k0 : a_rows, TA ? a_cols : a_cols - k0,
+                    guard, vec, gtid);
+            cb.load(b_ptr + kt * b_step, g.ldb, TB ? b_rows : b_rows - k0, TB ? b_cols - k0 : b_cols,
+                    guard, vec, gtid);
+        };
 
-    f32x16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    F f0, f1;
-    // Group grp takes k-tiles kt_begin + grp, + KG, ... In round r its k-tile
-    // is t = kt_begin + r*KG + grp. Invariant at the top of round r: the
-    // group's LDS buffer r&1 holds k-tile t (when t < kt_end) and f0 holds
-    // its q-group 0.
-    if (kt_begin + grp < kt_end) {
-        fetch_any(kt_begin + grp);
-        ca.store(a_lds, gtid);
-        cb.store(b_lds, gtid);
-    }
-    __syncthreads();
-    if (kt_begin + grp < kt_end) f0.template read<AS, BS>(a_lds, b_lds, 0, wm, wn, li, lh);
-
-    // Straight-line rounds (this and the next k-tile complete and in
-    // range) first, then the guarded ones, as two loops; the condition
-    // holds for a prefix of the rounds, and both kinds end on one barrier.
-    int r = 0;
-    if (wg_fast) {
-        for (; kt_begin + (r + 1) * KG + grp < kfast_end; ++r) {
-            const int cur = r & 1, nxt = cur ^ 1;
-            const float *as = a_lds + cur * A_FLOATS;
-            const float *bs = b_lds + cur * B_FLOATS;
-            float *as_n = a_lds + nxt * A_FLOATS;
-            float *bs_n = b_lds + nxt * B_FLOATS;
-            fetch_fast(kt_begin + (r + 1) * KG + grp);
-#pragma unroll
-            for (int q = 0; q < Q; q += 2) {
-                f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
-                f0.mma(acc);
-                if (q + 2 < Q) {
-                    f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
-                } else {
-                    ca.store(as_n, gtid);
-                    cb.store(bs_n, gtid);
-                }
-                f1.mma(acc);
-            }
-            // DS reads per q-group: FM (or FN) 16-byte reads of a k-contiguous
-            // tile, four narrow reads of an m/n-contiguous one.
-            schedule_iteration<4 * FM * FN, Q, ACopy::PER_THREAD + BCopy::PER_THREAD,
-                               (TA ? 4 : FM) + (TB ? FN : 4), ACopy::PER_THREAD + BCopy::PER_THREAD>();
-            __syncthreads();
-            f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
-        }
-    }
-    for (; r < rounds; ++r) {
-        const int t = kt_begin + r * KG + grp, tn_ = t + KG;
-        const int cur = r & 1, nxt = cur ^ 1;
-        const float *as = a_lds + cur * A_FLOATS;
-        const float *bs = b_lds + cur * B_FLOATS;
-        float *as_n = a_lds + nxt * A_FLOATS;
-        float *bs_n = b_lds + nxt * B_FLOATS;
-        const bool has_cur = t < kt_end, has_next = tn_ < kt_end;
-        if (has_next) fetch_any(tn_);
-        if (has_cur) {
-#pragma unroll
-            for (int q = 0; q < Q; q += 2) {
-                f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
-                f0.mma(acc);
-                if (q + 2 < Q) f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
-                f1.mma(acc);
-            }
-        }
-        if (has_next) {
-            ca.store(as_n, gtid);
-            cb.store(bs_n, gtid);
-        }
-        __syncthreads();
-        if (has_next) f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
-    }
-
-    if constexpr (KG > 1) {
-        // Groups 1..KG-1 hand their accumulators to group 0 through LDS (the
-        // tile buffers are free after the last barrier); group 0 adds them in
-        // group order, so the sum is the same on every call.
-        constexpr int SLOT = FM * FN * 16 * 64;            // floats per wave
-        constexpr int WAVES = NTG / 64;
-        if (grp > 0) {
-            float *dst = lds + ((grp - 1) * WAVES + wave) * SLOT + lane;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
-        }
-        __syncthreads();
-        // Without split-K no barrier follows, so the other groups are done.
-        if (!CFG::SPLIT && grp > 0) return;
-        if (grp == 0)
-#pragma unroll
-        for (int g2 = 1; g2 < KG; ++g2) {
-            const float *src = lds + ((g2 - 1) * WAVES + wave) * SLOT + lane;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
-        }
-    }
-
-    if constexpr (CFG::SPLIT) if (g.splits > 1) {
-        // Split-K over workgroups: store this partial tile (group 0's
-        // accumulators, in register order) to the workspace with system-scope
-        // stores, count in, and let the workgroup that completes the count sum
-        // the partials in split order before the epilogue. Same protocol as the
-        // skinny band kernel; every wave of the workgroup reaches each barrier.
-        constexpr int REGS = FM * FN * 16;
-        constexpr size_t PART = (size_t)BM * BN;
-        __shared__ int is_last;
-        const int S = g.splits;
-        const size_t tile_id = (size_t)tm * g.tiles_n + tn;
-        float *mine = g.ws + (tile_id * S + split) * PART + (size_t)wave * REGS * 64 + lane;
-        if (grp == 0) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        __hip_atomic_store(mine + ((i * FN + j) * 16 + r) * 64, acc[i][j][r], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_SYSTEM);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0)
-            is_last = __hip_atomic_fetch_add(&g.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
-                      S - 1;
-        __syncthreads();
-        if (!is_last) return;
-        const float *base = g.ws + tile_id * S * PART + (size_t)wave * REGS * 64 + lane;
+        f32x16 acc[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        // SB splits' loads in flight at a time (about 64 registers); the sum
-        // runs in split order.
-        constexpr int SB = REGS >= 64 ? 1 : 64 / REGS;
-        for (int sp0 = 0; sp0 < S; sp0 += SB) {
-            float v[SB][FM][FN][16];
+
+        F f0, f1;
+        // Group grp takes k-tiles kt_begin + grp, + KG, ... In round r its k-tile
+        // is t = kt_begin + r*KG + grp. Invariant at the top of round r: the
+        // group's LDS buffer r&1 holds k-tile t (when t < kt_end) and f0 holds
+        // its q-group 0.
+        if (kt_begin + grp < kt_end) {
+            fetch_any(kt_begin + grp);
+            ca.store(a_lds, gtid);
+            cb.store(b_lds, gtid);
+        }
+        __syncthreads();
+        if (kt_begin + grp < kt_end) f0.template read<AS, BS>(a_lds, b_lds, 0, wm, wn, li, lh);
+
+        // Straight-line rounds (this and the next k-tile complete and in
+        // range) first, then the guarded ones, as two loops; the condition
+        // holds for a prefix of the rounds, and both kinds end on one barrier.
+        int r = 0;
+        if (wg_fast) {
+            for (; kt_begin + (r + 1) * KG + grp < kfast_end; ++r) {
+                const int cur = r & 1, nxt = cur ^ 1;
+                const float *as = a_lds + cur * A_FLOATS;
+                const float *bs = b_lds + cur * B_FLOATS;
+                float *as_n = a_lds + nxt * A_FLOATS;
+                float *bs_n = b_lds + nxt * B_FLOATS;
+                fetch_fast(kt_begin + (r + 1) * KG + grp);
 #pragma unroll
-            for (int u = 0; u < SB; ++u)
+                for (int q = 0; q < Q; q += 2) {
+                    f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
+                    f0.mma(acc);
+                    if (q + 2 < Q) {
+                        f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
+                    } else {
+                        ca.store(as_n, gtid);
+                        cb.store(bs_n, gtid);
+                    }
+                    f1.mma(acc);
+                }
+                // DS reads per q-group: FM (or FN) 16-byte reads of a k-contiguous
+                // tile, four narrow reads of an m/n-contiguous one.
+                schedule_iteration<4 * FM * FN, Q, ACopy::PER_THREAD + BCopy::PER_THREAD,
+                                   (TA ? 4 : FM) + (TB ? FN : 4), ACopy::PER_THREAD + BCopy::PER_THREAD>();
+                __syncthreads();
+                f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
+            }
+        }
+        for (; r < rounds; ++r) {
+            const int t = kt_begin + r * KG + grp, tn_ = t + KG;
+            const int cur = r & 1, nxt = cur ^ 1;
+            const float *as = a_lds + cur * A_FLOATS;
+            const float *bs = b_lds + cur * B_FLOATS;
+            float *as_n = a_lds + nxt * A_FLOATS;
+            float *bs_n = b_lds + nxt * B_FLOATS;
+            const bool has_cur = t < kt_end, has_next = tn_ < kt_end;
+            if (has_next) fetch_any(tn_);
+            if (has_cur) {
+#pragma unroll
+                for (int q = 0; q < Q; q += 2) {
+                    f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
+                    f0.mma(acc);
+                    if (q + 2 < Q) f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
+                    f1.mma(acc);
+                }
+            }
+            if (has_next) {
+                ca.store(as_n, gtid);
+                cb.store(bs_n, gtid);
+            }
+            __syncthreads();
+            if (has_next) f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
+        }
+
+        if constexpr (KG > 1) {
+            // Groups 1..KG-1 hand their accumulators to group 0 through LDS (the
+            // tile buffers are free after the last barrier); group 0 adds them in
+            // group order, so the sum is the same on every call.
+            constexpr int SLOT = FM * FN * 16 * 64;            // floats per wave
+            constexpr int WAVES = NTG / 64;
+            if (grp > 0) {
+                float *dst = lds + ((grp - 1) * WAVES + wave) * SLOT + lane;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+            }
+            __syncthreads();
+            // Without split-K no barrier follows, so the other groups are done.
+            if (!CFG::SPLIT && grp > 0) return;
+            if (grp == 0)
+#pragma unroll
+            for (int g2 = 1; g2 < KG; ++g2) {
+                const float *src = lds + ((g2 - 1) * WAVES + wave) * SLOT + lane;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
+            }
+        }
+
+        if constexpr (CFG::SPLIT || CFG::STREAMK) if (sg.nseg > 1) {
+            // Split-K over workgroups: store this partial tile (group 0's
+            // accumulators, in register order) to the workspace with system-scope
+            // stores, count in, and let the workgroup that completes the count sum
+            // the partials in split order before the epilogue. Same protocol as the
+            // skinny band kernel; every wave of the workgroup reaches each barrier.
+            constexpr int REGS = FM * FN * 16;
+            constexpr size_t PART = (size_t)BM * BN;
+            const int S = sg.nseg;
+            const size_t tile_id = (size_t)sg.counter;
+            float *mine = g.ws + (size_t)sg.slot(sg.seg) * PART + (size_t)wave * REGS * 64 + lane;
+            if (grp == 0) {
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
-                            v[u][i][j][r] = (grp == 0 && sp0 + u < S)
-                                                ? __hip_atomic_load(base + (size_t)(sp0 + u) * PART +
-                                                                        ((i * FN + j) * 16 + r) * 64,
-                                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
-                                                : 0.0f;
+                            __hip_atomic_store(mine + ((i * FN + j) * 16 + r) * 64, acc[i][j][r], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0)
+                is_last = __hip_atomic_fetch_add(&g.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                          S - 1;
+            __syncthreads();
+            if (!is_last) return;
+            const float *base = g.ws + (size_t)wave * REGS * 64 + lane;
 #pragma unroll
-            for (int u = 0; u < SB; ++u)
-                if (sp0 + u < S)
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            // SB splits' loads in flight at a time (about 64 registers); the sum
+            // runs in split order.
+            constexpr int SB = (REGS >= 64 || CFG::WAVES_PER_EU > 2) ? 1 : 64 / REGS;
+            for (int sp0 = 0; sp0 < S; sp0 += SB) {
+                float v[SB][FM][FN][16];
+#pragma unroll
+                for (int u = 0; u < SB; ++u)
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) acc[i][j][r] += v[u][i][j][r];
+                            for (int r = 0; r < 16; ++r)
+                                v[u][i][j][r] = (grp == 0 && sp0 + u < S)
+                                                    ? __hip_atomic_load(base + (size_t)sg.slot(sp0 + u) * PART +
+                                                                            ((i * FN + j) * 16 + r) * 64,
+                                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                                                    : 0.0f;
+#pragma unroll
+                for (int u = 0; u < SB; ++u)
+                    if (sp0 + u < S)
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) acc[i][j][r] += v[u][i][j][r];
+            }
+            if (tid == 0) __hip_atomic_store(&g.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
-        if (tid == 0) __hip_atomic_store(&g.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    if (grp > 0) return;
+        if (grp > 0) return;
 
-    // Epilogue. Accumulator element r of block (i, j) in lane (li, lh) is
-    // block row 8*(r/4) + 4*lh + r%4, block column li.
-    const float alpha = g.alpha, beta = g.beta;
-    float *const cw = g.C + (size_t)(m0 + wm * WTM) * g.ldc + (n0 + wn * WTN);
-    const int rows_left = M - (m0 + wm * WTM), cols_left = N - (n0 + wn * WTN);
-    const int ldc = g.ldc;
+        // Epilogue. Accumulator element r of block (i, j) in lane (li, lh) is
+        // block row 8*(r/4) + 4*lh + r%4, block column li.
+        const float alpha = g.alpha, beta = g.beta;
+        float *const cw = g.C + (size_t)(m0 + wm * WTM) * g.ldc + (n0 + wn * WTN);
+        const int rows_left = M - (m0 + wm * WTM), cols_left = N - (n0 + wn * WTN);
+        const int ldc = g.ldc;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ib = 8 * (r / 4) + 4 * lh + (r % 4);
-            const int row = TA ? FM * ib + i : 32 * i + ib;
-            if (row >= rows_left) continue;
-            float *crow = cw + (size_t)row * ldc;
-            if (!TB) {
-                // FN adjacent columns FN*li .. FN*li + FN-1.
-                const int col = FN * li;
-                float out[FN];
+            for (int r = 0; r < 16; ++r) {
+                const int ib = 8 * (r / 4) + 4 * lh + (r % 4);
+                const int row = TA ? FM * ib + i : 32 * i + ib;
+                if (row >= rows_left) continue;
+                float *crow = cw + (size_t)row * ldc;
+                if (!TB) {
+                    // FN adjacent columns FN*li .. FN*li + FN-1.
+                    const int col = FN * li;
+                    float out[FN];
 #pragma unroll
-                for (int j = 0; j < FN; ++j) out[j] = alpha * acc[i][j][r];
-                store_run<FN>(crow + col, out, beta, g.vec_c && col + FN <= cols_left, cols_left - col);
-            } else {
+                    for (int j = 0; j < FN; ++j) out[j] = alpha * acc[i][j][r];
+                    store_run<FN>(crow + col, out, beta, g.vec_c && col + FN <= cols_left, cols_left - col);
+                } else {
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int col = 32 * j + li;
-                    if (col < cols_left) {
-                        float *p = crow + col;
-                        const float o = alpha * acc[i][j][r];
-                        *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
+                    for (int j = 0; j < FN; ++j) {
+                        const int col = 32 * j + li;
+                        if (col < cols_left) {
+                            float *p = crow + col;
+                            const float o = alpha * acc[i][j][r];
+                            *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
+                        }
                     }
                 }
             }
         }
+    };
+
+    if constexpr (CFG::STREAMK) {
+        static_assert(KG == 1 && !CFG::SPLIT, "stream-K runs one k-group");
+        // Iteration i is k-tile i % ktiles of tile i / ktiles (tiles in the
+        // grouped order). Workgroup w owns [start(w), start(w+1)); workgroups
+        // on one XCD own consecutive shares, so neighbouring tiles share its L2.
+        // A tile cut between workgroups w0..w1 has one segment per workgroup.
+        // Workgroup w keeps the partial of its first tile in slot 2w and of
+        // its last in slot 2w+1; segment j > 0 of a tile always starts its
+        // workgroup's share, so its slot is 2(w0+j).
+        const long long G = gridDim.x;
+        const long long total = (long long)g.tiles_m * g.tiles_n * ktiles;
+        auto start = [&](long long w) { return w * total / G; };
+        auto owner = [&](long long i) { return ((i + 1) * G + total - 1) / total - 1; };
+        const int w = xcd_logical();
+        long long it = start(w);
+        const long long it_end = start(w + 1);
+        while (it < it_end) {
+            const int t = (int)(it / ktiles);
+            const long long t0 = (long long)t * ktiles;
+            const int kb = (int)(it - t0);
+            const int ke = (int)min((long long)ktiles, kb + (it_end - it));
+            SegInfo sg;
+            sg.counter = t;
+            sg.sstep = 2;
+            if (kb == 0 && ke == ktiles) {
+                sg.nseg = 1;
+                sg.seg = 0;
+                sg.s0 = sg.sbase = 0;
+            } else {
+                const int w0 = (int)owner(t0), w1 = (int)owner(t0 + ktiles - 1);
+                sg.nseg = w1 - w0 + 1;
+                sg.seg = w - w0;
+                sg.sbase = 2 * w0;
+                sg.s0 = 2 * w0 + (start(w0) < t0 ? 1 : 0);
+            }
+            int tm, tn;
+            tile_of(t, g.tiles_m, g.tiles_n, tm, tn);
+            run_tile(tm, tn, kb, ke, sg);
+            it += ke - kb;
+        }
+    } else {
+        int tm, tn, split;
+        tile_coords(g.tiles_m, g.tiles_n, CFG::SPLIT ? g.splits : 1, tm, tn, split);
+        SegInfo sg;
+        sg.nseg = CFG::SPLIT ? g.splits : 1;
+        sg.seg = split;
+        sg.counter = tm * g.tiles_n + tn;
+        sg.s0 = sg.sbase = sg.counter * sg.nseg;
+        sg.sstep = 1;
+        const int kt_begin = CFG::SPLIT ? split * g.kt_per_split : 0;
+        const int kt_end = CFG::SPLIT ? min(ktiles, kt_begin + g.kt_per_split) : ktiles;
+        run_tile(tm, tn, kt_begin, kt_end, sg);
     }
 }
 
@@ -1078,9 +1159,12 @@ using CfgT = TileCfg<128, 256, 32, 2, 4>;        // 8 waves, 64 x 64 per wave
 using CfgT16 = TileCfg<128, 256, 16, 2, 2>;      // 4 waves, 64 x 128 per wave, 2 per CU
 using CfgQ32 = TileCfg<256, 256, 32, 4, 2>;      // 8 waves, 64 x 128 per wave, 1 per CU
 // Split-K over workgroups (for grids with fewer tiles than CU slots).
-using CfgL42K = TileCfg<128, 128, 32, 4, 2, 1, 4, true>;
+using CfgL42K = TileCfg<128, 128, 32, 4, 2, 1, 0, true>;
 using CfgSK = TileCfg<64, 64, 32, 2, 2, 1, 0, true>;
 using CfgLK = TileCfg<128, 128, 32, 2, 2, 1, 0, true>;
+// Stream-K: one workgroup per CU (two waves per SIMD), or two (four).
+using CfgL42S1 = TileCfg<128, 128, 32, 4, 2, 1, 2, false, true>;
+using CfgL42S2 = TileCfg<128, 128, 32, 4, 2, 1, 4, false, true>;
 
 struct ConfigInfo {
     const char *name;
@@ -1104,6 +1188,8 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_128x128x32_w2x2_splitk", CfgLK::BM, CfgLK::BN, CfgLK::NT},
     {"mfma32_128x256x16_w2x2", CfgT16::BM, CfgT16::BN, CfgT16::NT},
     {"mfma32_256x256x32_w4x2", CfgQ32::BM, CfgQ32::BN, CfgQ32::NT},
+    {"mfma32_128x128x32_w4x2_streamk_1wg", CfgL42S1::BM, CfgL42S1::BN, CfgL42S1::NT},
+    {"mfma32_128x128x32_w4x2_streamk_2wg", CfgL42S2::BM, CfgL42S2::BN, CfgL42S2::NT},
 };
 constexpr int kSkinnyConfig = 2;
 constexpr int kBandConfig = 3;
@@ -1150,6 +1236,8 @@ double cu_balance(long long tiles, int slots = 1) {
 //   >= 256 tiles of 128 x 128: the best-scoring of
 //                       256 x 256 with 8 waves (one per CU; B not
 //                         transposed)                        1.044 x balance
+//                       stream-K 128 x 128, two workgroups per CU
+//                         (>= 8 k-tiles per workgroup)       0.925 (always balanced)
 //                       128 x 256 with 4 waves (two workgroups per CU; B
 //                         not transposed)                    1.038 x balance over 2 slots per CU
 //                       256 x 128 / 128 x 256 with 8 waves (one per CU; B
@@ -1158,7 +1246,9 @@ double cu_balance(long long tiles, int slots = 1) {
 //                       64 x 64                               0.87 x balance
 //                       (the factors are their relative speeds on a large,
 //                       evenly spread product);
-//   192..255 such tiles 128 x 128 with 8 waves;
+//   144..255 such tiles with >= 20 k-tiles per workgroup: stream-K 128 x 128,
+//                       one workgroup per CU;
+//   192..255 such tiles otherwise: 128 x 128 with 8 waves;
 //   else, by 64 x 64 tiles: >= 512 plain; 257..511 two k-groups, or split-K
 //                       over workgroups when those would fill under 70% of
 //                       the CU slots; <= 96 split-K over workgroups; else
@@ -1169,6 +1259,8 @@ int select_config(char transA, char transB, int M, int N, int K) {
     if (M <= kSkinnyMaxM) return kBandConfig;
     auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const long long t128 = tiles(128, 128), t64 = tiles(64, 64);
+    // Stream-K work: 128 x 128 x 32 iterations.
+    const long long sk_iters = t128 * ((K + 31) / 32);
     if (t128 >= kNumCus) {
         const bool tb = op_t(transB);
         const bool tall = M >= N;
@@ -1176,12 +1268,18 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const double s_b4 = tb ? -1.0 : 1.038 * cu_balance(tiles(128, 256), 2);
         const double s_b8 = tb ? -1.0 : 1.024 * cu_balance(tall ? tiles(256, 128) : tiles(128, 256));
         const double s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
-        const double best = fmax(fmax(s_q, fmax(s_b4, s_b8)), fmax(s_128, s_64));
+        // Stream-K fills every CU slot whatever the tile count.
+        const double s_sk = sk_iters >= 8LL * 2 * kNumCus ? 0.925 : -1.0;
+        const double best = fmax(fmax(fmax(s_q, s_sk), fmax(s_b4, s_b8)), fmax(s_128, s_64));
         if (best == s_q) return 15;
+        if (best == s_sk) return 17;
         if (best == s_b4) return 14;
         if (best == s_b8) return tall ? 9 : 10;
         return best == s_128 ? 8 : 1;
     }
+    // 144..255 tiles of 128 x 128 with at least 20 k-tiles per workgroup:
+    // stream-K, one workgroup per CU.
+    if (t128 >= 144 && sk_iters >= 20LL * kNumCus) return 16;
     if (t128 >= 3 * kNumCus / 4) return 8;
     if (t64 >= 2 * kNumCus) return 1;
     // 257..511 tiles of 64 x 64: two k-groups unless their workgroups would
@@ -1196,8 +1294,8 @@ int select_config(char transA, char transB, int M, int N, int K) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 template <class CFG, bool TA, bool TB>
-hipError_t launch_t(const GemmArgs &g, hipStream_t stream) {
-    dim3 grid((unsigned)(g.tiles_m * g.tiles_n * g.splits));
+hipError_t launch_t(const GemmArgs &g, unsigned workgroups, hipStream_t stream) {
+    dim3 grid(workgroups);
     dim3 block(CFG::NT);
     hipLaunchKernelGGL((sgemm_mfma32<CFG, TA, TB>), grid, block, 0, stream, g);
     return hipGetLastError();
@@ -1206,7 +1304,7 @@ hipError_t launch_t(const GemmArgs &g, hipStream_t stream) {
 // Workspace for the split-K reduction, one per (device, stream) so that calls
 // on different streams never share partials or counters. Allocated on the
 // first call that needs it and kept until the process ends.
-constexpr size_t kWsFloats = size_t(8) << 20;   // 32 MiB of partial blocks
+constexpr size_t kWsFloats = size_t(16) << 20;  // 64 MiB of partial blocks
 constexpr int kWsCounters = 1 << 16;
 
 struct Workspace {
@@ -1361,10 +1459,32 @@ hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int spl
         g.splits = (int)S;
         if (g.splits == 1) g.kt_per_split = ktiles;
     }
-    if (!ta && !tb) return launch_t<CFG, false, false>(g, stream);
-    if (!ta && tb) return launch_t<CFG, false, true>(g, stream);
-    if (ta && !tb) return launch_t<CFG, true, false>(g, stream);
-    return launch_t<CFG, true, true>(g, stream);
+    unsigned workgroups = (unsigned)((long long)g.tiles_m * g.tiles_n * g.splits);
+    if constexpr (CFG::STREAMK) {
+        // One workgroup per CU, each owning an equal share of the tiles x
+        // k-tiles iterations; each keeps at most two partial blocks (its first
+        // and last tile) and every tile has one counter. When the shares cut
+        // no tile (tiles a multiple of the grid) no workspace is needed; when
+        // it is needed but missing, every workgroup takes one whole tile.
+        const long long tiles = (long long)g.tiles_m * g.tiles_n;
+        const long long per_cu = std::max(1, CFG::WAVES_PER_EU * 4 * 64 / CFG::NT);
+        long long G = std::min(tiles * ktiles, (long long)kNumCus * per_cu);
+        G = std::min(G, (long long)(kWsFloats / ((size_t)2 * CFG::BM * CFG::BN)));
+        if (tiles % G != 0) {
+            const Workspace *w = tiles <= kWsCounters ? get_workspace(stream) : nullptr;
+            if (w == nullptr) {
+                G = tiles;
+            } else {
+                g.ws = w->partials;
+                g.counters = w->counters;
+            }
+        }
+        workgroups = (unsigned)G;
+    }
+    if (!ta && !tb) return launch_t<CFG, false, false>(g, workgroups, stream);
+    if (!ta && tb) return launch_t<CFG, false, true>(g, workgroups, stream);
+    if (ta && !tb) return launch_t<CFG, true, false>(g, workgroups, stream);
+    return launch_t<CFG, true, true>(g, workgroups, stream);
 }
 
 int run(int config, char transA, char transB, int M, int N, int K, float alpha, const float *A, int lda,
@@ -1426,7 +1546,9 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case 12: err = launch_cfg<CfgSK>(ta, tb, g, stream, 2); break;
         case 13: err = launch_cfg<CfgLK>(ta, tb, g, stream, 1); break;
         case 14: err = launch_cfg<CfgT16>(ta, tb, g, stream); break;
-        default: err = launch_cfg<CfgQ32>(ta, tb, g, stream); break;
+        case 15: err = launch_cfg<CfgQ32>(ta, tb, g, stream); break;
+        case 16: err = launch_cfg<CfgL42S1>(ta, tb, g, stream); break;
+        default: err = launch_cfg<CfgL42S2>(ta, tb, g, stream); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }

@@ -126,12 +126,16 @@ def test_shape_class_selection():
     assert sel("N", "N", 1280, 1280, 1280) == "mfma32_64x64x32_w2x2_kg2"
     assert sel("N", "N", 512, 512, 512) == "mfma32_64x64x32_w2x2_splitk"
     assert sel("N", "N", 768, 768, 768) == "mfma32_64x64x32_w2x2_kg4"
-    assert sel("N", "N", 1792, 1792, 1792) == "mfma32_128x128x32_w4x2"
-    assert sel("N", "N", 1536, 1536, 1536) == "mfma32_64x64x32_w2x2"
+    # 144..255 tiles of 128 x 128 with enough k-work: stream-K, one workgroup per CU.
+    assert sel("N", "N", 1792, 1792, 1792) == "mfma32_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "N", 1536, 1536, 1536) == "mfma32_128x128x32_w4x2_streamk_1wg"
+    # ... but not with little k-work per workgroup.
+    assert sel("N", "N", 1536, 1536, 256) == "mfma32_64x64x32_w2x2"
     # Square sizes: whichever tile spreads most evenly over the 256 CUs.
-    for n, want in [(2048, "128x128x32_w4x2"), (2304, "64x64x32_w2x2"), (2560, "256x128x32_w4x2"),
-                    (2816, "256x128x32_w4x2"), (3072, "64x64x32_w2x2"), (3328, "128x128x32_w4x2"),
-                    (3584, "64x64x32_w2x2"), (3840, "256x256x32_w4x2"), (4096, "256x256x32_w4x2"),
+    # Stream-K (two workgroups per CU) where no tile spreads evenly.
+    sk2 = "128x128x32_w4x2_streamk_2wg"
+    for n, want in [(2048, "128x128x32_w4x2"), (2304, sk2), (2560, sk2), (2816, "256x128x32_w4x2"), (3072, sk2),
+                    (3328, sk2), (3584, sk2), (3840, sk2), (4096, "256x256x32_w4x2"),
                     (8192, "256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == "mfma32_" + want, n
     # M <= 32: the skinny, bandwidth-bound kernel.

@@ -232,6 +232,54 @@ def test_band_concurrent_streams():
     assert all(np.array_equal(C.cpu().numpy().view(np.uint32), ref) for C in outs)
 
 
+# --- split-K and stream-K tile kernels -----------------------------------------------------
+
+_NAMES = mg.config_names()
+STREAMK = [_NAMES.index(n) for n in ("mfma32_128x128x32_w4x2_streamk_1wg", "mfma32_128x128x32_w4x2_streamk_2wg")]
+SPLIT_TILE = [i for i, n in enumerate(_NAMES) if n.startswith("mfma32_") and n.endswith("_splitk")]
+
+
+@pytest.mark.parametrize("config", STREAMK + SPLIT_TILE)
+@pytest.mark.parametrize("ta,tb", OPS)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 4096),    # 4 tiles, each cut across dozens of workgroups
+                                   (1000, 1300, 700),   # ragged edges, tiles cut mid-k
+                                   (129, 1000, 3001),   # ragged k tail inside a cut tile
+                                   (2304, 2304, 96)])   # many tiles, three k-tiles each
+def test_split_and_stream_k_integer(config, ta, tb, M, N, K):
+    """Tiles whose k-range is cut between workgroups: integer inputs, so the
+    result is bit-exact whatever the cut and the partial-sum order."""
+    case = W.Case(f"sk_{ta}{tb}_{M}x{N}x{K}_cfg{config}", ta, tb, M, N, K, 1.0, -1.0, seed=70 + K % 7,
+                  fill="int_rand")
+    note(case.name)
+    inp = W.make_inputs(case)
+    compare(case, run_gpu(case, inp, config=config), run_oracle(case, inp), True)
+
+
+@pytest.mark.parametrize("config", STREAMK)
+def test_stream_k_deterministic_and_concurrent(config):
+    """Stream-K on uniform data: within tolerance of the oracle, and twenty
+    calls over two concurrent streams (each with its own workspace) give
+    identical bits."""
+    case = W.Case(f"sk_det_cfg{config}", "N", "N", 1000, 1300, 700, 1.0, 0.0, seed=71)
+    note(case.name)
+    inp = W.make_inputs(case)
+    A = torch.from_numpy(inp.A).cuda()
+    B = torch.from_numpy(inp.B).cuda()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(10):
+        for st in (s1, s2):
+            C = torch.full((case.M, case.N), float("nan"), device="cuda")
+            C.record_stream(st)
+            mg.sgemm("N", "N", 1.0, A, B, 0.0, C, stream=st.cuda_stream, config=config)
+            outs.append(C)
+    torch.cuda.synchronize()
+    ref = outs[0].cpu().numpy()
+    compare(case, ref, run_oracle(case, inp), False)
+    assert all(np.array_equal(C.cpu().numpy().view(np.uint32), ref.view(np.uint32)) for C in outs)
+
+
 # --- every kernel configuration on ragged shapes ------------------------------------------
 
 def _edge_triples(count, seed):
