@@ -1165,6 +1165,8 @@ using CfgLK = TileCfg<128, 128, 32, 2, 2, 1, 0, true>;
 // Stream-K: one workgroup per CU (two waves per SIMD), or two (four).
 using CfgL42S1 = TileCfg<128, 128, 32, 4, 2, 1, 2, false, true>;
 using CfgL42S2 = TileCfg<128, 128, 32, 4, 2, 1, 4, false, true>;
+using CfgWS = TileCfg<256, 128, 32, 4, 2, 1, 0, false, true>;   // one workgroup per CU
+using CfgTS = TileCfg<128, 256, 32, 2, 4, 1, 0, false, true>;
 
 struct ConfigInfo {
     const char *name;
@@ -1190,6 +1192,8 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_256x256x32_w4x2", CfgQ32::BM, CfgQ32::BN, CfgQ32::NT},
     {"mfma32_128x128x32_w4x2_streamk_1wg", CfgL42S1::BM, CfgL42S1::BN, CfgL42S1::NT},
     {"mfma32_128x128x32_w4x2_streamk_2wg", CfgL42S2::BM, CfgL42S2::BN, CfgL42S2::NT},
+    {"mfma32_256x128x32_w4x2_streamk", CfgWS::BM, CfgWS::BN, CfgWS::NT},
+    {"mfma32_128x256x32_w2x4_streamk", CfgTS::BM, CfgTS::BN, CfgTS::NT},
 };
 constexpr int kSkinnyConfig = 2;
 constexpr int kBandConfig = 3;
@@ -1236,8 +1240,10 @@ double cu_balance(long long tiles, int slots = 1) {
 //   >= 256 tiles of 128 x 128: the best-scoring of
 //                       256 x 256 with 8 waves (one per CU; B not
 //                         transposed)                        1.044 x balance
+//                       stream-K 256 x 128 / 128 x 256, one workgroup
+//                         per CU (B not transposed)          0.955 (always balanced)
 //                       stream-K 128 x 128, two workgroups per CU
-//                         (>= 8 k-tiles per workgroup)       0.925 (always balanced)
+//                         (either: >= 8 k-tiles per workgroup) 0.925 (always balanced)
 //                       128 x 256 with 4 waves (two workgroups per CU; B
 //                         not transposed)                    1.038 x balance over 2 slots per CU
 //                       256 x 128 / 128 x 256 with 8 waves (one per CU; B
@@ -1268,10 +1274,14 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const double s_b4 = tb ? -1.0 : 1.038 * cu_balance(tiles(128, 256), 2);
         const double s_b8 = tb ? -1.0 : 1.024 * cu_balance(tall ? tiles(256, 128) : tiles(128, 256));
         const double s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
-        // Stream-K fills every CU slot whatever the tile count.
-        const double s_sk = sk_iters >= 8LL * 2 * kNumCus ? 0.925 : -1.0;
-        const double best = fmax(fmax(fmax(s_q, s_sk), fmax(s_b4, s_b8)), fmax(s_128, s_64));
+        // Stream-K fills every CU slot whatever the tile count: with the
+        // 256 x 128 / 128 x 256 tile (B not transposed), else 128 x 128.
+        const bool sk_ok = sk_iters >= 8LL * 2 * kNumCus;
+        const double s_skb = (sk_ok && !tb) ? 0.955 : -1.0;
+        const double s_sk = sk_ok ? 0.925 : -1.0;
+        const double best = fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(s_128, s_64));
         if (best == s_q) return 15;
+        if (best == s_skb) return tall ? 18 : 19;
         if (best == s_sk) return 17;
         if (best == s_b4) return 14;
         if (best == s_b8) return tall ? 9 : 10;
@@ -1548,7 +1558,9 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case 14: err = launch_cfg<CfgT16>(ta, tb, g, stream); break;
         case 15: err = launch_cfg<CfgQ32>(ta, tb, g, stream); break;
         case 16: err = launch_cfg<CfgL42S1>(ta, tb, g, stream); break;
-        default: err = launch_cfg<CfgL42S2>(ta, tb, g, stream); break;
+        case 17: err = launch_cfg<CfgL42S2>(ta, tb, g, stream); break;
+        case 18: err = launch_cfg<CfgWS>(ta, tb, g, stream); break;
+        default: err = launch_cfg<CfgTS>(ta, tb, g, stream); break;
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }

@@ -132,12 +132,17 @@ def test_shape_class_selection():
     # ... but not with little k-work per workgroup.
     assert sel("N", "N", 1536, 1536, 256) == "mfma32_64x64x32_w2x2"
     # Square sizes: whichever tile spreads most evenly over the 256 CUs.
-    # Stream-K (two workgroups per CU) where no tile spreads evenly.
-    sk2 = "128x128x32_w4x2_streamk_2wg"
-    for n, want in [(2048, "128x128x32_w4x2"), (2304, sk2), (2560, sk2), (2816, "256x128x32_w4x2"), (3072, sk2),
-                    (3328, sk2), (3584, sk2), (3840, sk2), (4096, "256x256x32_w4x2"),
+    # Stream-K over 256 x 128 tiles where no data-parallel tile spreads evenly.
+    skw = "256x128x32_w4x2_streamk"
+    for n, want in [(2048, "128x128x32_w4x2"), (2304, skw), (2560, skw), (2816, "256x128x32_w4x2"), (3072, skw),
+                    (3328, skw), (3584, skw), (3840, skw), (4096, "256x256x32_w4x2"),
                     (8192, "256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == "mfma32_" + want, n
+    # B transposed: no big tiles, so stream-K runs 128 x 128 tiles, two per CU.
+    assert sel("N", "T", 3072, 3072, 3072) == "mfma32_128x128x32_w4x2_streamk_2wg"
+    assert sel("T", "T", 2560, 2560, 2560) == "mfma32_128x128x32_w4x2_streamk_2wg"
+    # N > M: the 128 x 256 stream-K tile.
+    assert sel("N", "N", 2304, 3328, 2048) == "mfma32_128x256x32_w2x4_streamk"
     # M <= 32: the skinny, bandwidth-bound kernel.
     assert "skinny" in sel("N", "N", 16, 4096, 4096)
     assert "skinny" in sel("T", "T", 32, 100, 7)

@@ -235,7 +235,8 @@ def test_band_concurrent_streams():
 # --- split-K and stream-K tile kernels -----------------------------------------------------
 
 _NAMES = mg.config_names()
-STREAMK = [_NAMES.index(n) for n in ("mfma32_128x128x32_w4x2_streamk_1wg", "mfma32_128x128x32_w4x2_streamk_2wg")]
+STREAMK = [_NAMES.index(n) for n in ("mfma32_128x128x32_w4x2_streamk_1wg", "mfma32_128x128x32_w4x2_streamk_2wg",
+                                     "mfma32_256x128x32_w4x2_streamk", "mfma32_128x256x32_w2x4_streamk")]
 SPLIT_TILE = [i for i, n in enumerate(_NAMES) if n.startswith("mfma32_") and n.endswith("_splitk")]
 
 
@@ -270,8 +271,8 @@ def test_stream_k_deterministic_and_concurrent(config):
     outs = []
     for rep in range(10):
         for st in (s1, s2):
-            C = torch.full((case.M, case.N), float("nan"), device="cuda")
-            C.record_stream(st)
+            with torch.cuda.stream(st):      # the NaN fill runs on st, before the product
+                C = torch.full((case.M, case.N), float("nan"), device="cuda")
             mg.sgemm("N", "N", 1.0, A, B, 0.0, C, stream=st.cuda_stream, config=config)
             outs.append(C)
     torch.cuda.synchronize()
