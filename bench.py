@@ -219,6 +219,30 @@ def run_table(path, steps, warmup):
             del prob
 
 
+def run_workload(name, steps, warmup):
+    """One workload with its chosen kernel: one JSON line of its numbers."""
+    import fp32_gemm_nn_amd as mg
+    from synthetic import workloads as W
+
+    cases = {c.name: c for c in [*W.all_cases(), *[W.c3(n) for n in W.C3_SIZES]]}
+    if name not in cases:
+        raise SystemExit(f"unknown workload {name!r}; one of: {', '.join(sorted(cases))}")
+    case = cases[name]
+    skinny = case.M <= 32
+    prob = Problem(case, copies=8 if skinny else 1)
+    _, ev = time_problem(prob, steps, warmup)
+    per = ev / steps
+    row = {"workload": case.name, "transA": case.transA, "transB": case.transB, "M": case.M, "N": case.N,
+           "K": case.K, "kernel_config": mg.mi_sgemm_config_name(
+               mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)),
+           "steps": steps, "us_per_call": round(per * 1e6, 3), "TFLOPS": round(tflops(case.flops, per), 3),
+           "pct_fp32_matrix_peak": round(100 * tflops(case.flops, per) / PEAK_FP32_MATRIX_TFLOPS, 2),
+           "GBps_algorithmic": round(case.algorithmic_bytes / per / 1e9, 1)}
+    if skinny:
+        row["pct_hbm_peak"] = round(100 * case.algorithmic_bytes / per / 1e9 / PEAK_HBM_GBPS, 2)
+    print(json.dumps(row), flush=True)
+
+
 def run_config_sweep(path, warmup=3):
     """Every kernel configuration on every workload (one JSON object per line):
     the data the shape-class rule in select_config is chosen from."""
@@ -255,6 +279,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep-configs", metavar="PATH",
                     help="also time every kernel configuration on every workload, to PATH")
+    ap.add_argument("--workload", metavar="NAME",
+                    help="time only this workload (a name from synthetic/workloads.py) with its chosen "
+                         "kernel and print its numbers; for profiling one configuration at a time")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -274,6 +301,9 @@ def main():
 
     if args.mode == "copy":
         run_copy(args.steps, args.warmup)
+        return
+    if args.workload:
+        run_workload(args.workload, args.steps, args.warmup)
         return
 
     case = W.HEADLINE

@@ -60,6 +60,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
+// Memory scope of the split-K exchange (partial blocks, counters): the
+// workgroups that meet there all run on this GPU.
+constexpr int kExchangeScope = __HIP_MEMORY_SCOPE_AGENT;
 constexpr int kLdsPad = 4;
 
 struct GemmArgs {
@@ -76,6 +79,9 @@ struct GemmArgs {
     // each taking `kt_per_split` consecutive k-tiles; with splits > 1 their
     // partial tiles meet in `ws` and `counters` (one counter per tile).
     int splits, kt_per_split;
+    // Stream-K: the last sk_dp_tiles tiles (a multiple of the grid) are taken
+    // whole, one per workgroup per wave, after the shared-out ones.
+    int sk_dp_tiles;
     float *ws;
     int *counters;
 };
@@ -539,7 +545,7 @@ void sgemm_mfma32(GemmArgs g) {
 
         if constexpr (CFG::SPLIT || CFG::STREAMK) if (sg.nseg > 1) {
             // Split-K over workgroups: store this partial tile (group 0's
-            // accumulators, in register order) to the workspace with system-scope
+            // accumulators, in register order) to the workspace with device-scope
             // stores, count in, and let the workgroup that completes the count sum
             // the partials in split order before the epilogue. Same protocol as the
             // skinny band kernel; every wave of the workgroup reaches each barrier.
@@ -556,12 +562,12 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
                             __hip_atomic_store(mine + ((i * FN + j) * 16 + r) * 64, acc[i][j][r], __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_SYSTEM);
+                                               kExchangeScope);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (tid == 0)
-                is_last = __hip_atomic_fetch_add(&g.counters[tile_id], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                is_last = __hip_atomic_fetch_add(&g.counters[tile_id], 1, __ATOMIC_RELAXED, kExchangeScope) ==
                           S - 1;
             __syncthreads();
             if (!is_last) return;
@@ -588,7 +594,7 @@ void sgemm_mfma32(GemmArgs g) {
                                 v[u][i][j][r] = (grp == 0 && sp0 + u < S)
                                                     ? __hip_atomic_load(base + (size_t)sg.slot(sp0 + u) * PART +
                                                                             ((i * FN + j) * 16 + r) * 64,
-                                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                                                                        __ATOMIC_RELAXED, kExchangeScope)
                                                     : 0.0f;
 #pragma unroll
                 for (int u = 0; u < SB; ++u)
@@ -600,7 +606,7 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
                                 for (int r = 0; r < 16; ++r) acc[i][j][r] += v[u][i][j][r];
             }
-            if (tid == 0) __hip_atomic_store(&g.counters[tile_id], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (tid == 0) __hip_atomic_store(&g.counters[tile_id], 0, __ATOMIC_RELAXED, kExchangeScope);
         }
         if (grp > 0) return;
 
@@ -642,15 +648,17 @@ void sgemm_mfma32(GemmArgs g) {
 
     if constexpr (CFG::STREAMK) {
         static_assert(KG == 1 && !CFG::SPLIT, "stream-K runs one k-group");
-        // Iteration i is k-tile i % ktiles of tile i / ktiles (tiles in the
-        // grouped order). Workgroup w owns [start(w), start(w+1)); workgroups
-        // on one XCD own consecutive shares, so neighbouring tiles share its L2.
+        // The first sk_tiles tiles are shared out: iteration i is k-tile
+        // i % ktiles of tile i / ktiles (tiles in the grouped order), and
+        // workgroup w owns [start(w), start(w+1)); workgroups on one XCD own
+        // consecutive shares. The rest follow whole, one per workgroup per wave.
         // A tile cut between workgroups w0..w1 has one segment per workgroup.
         // Workgroup w keeps the partial of its first tile in slot 2w and of
         // its last in slot 2w+1; segment j > 0 of a tile always starts its
         // workgroup's share, so its slot is 2(w0+j).
         const long long G = gridDim.x;
-        const long long total = (long long)g.tiles_m * g.tiles_n * ktiles;
+        const int tiles = g.tiles_m * g.tiles_n, sk_tiles = tiles - g.sk_dp_tiles;
+        const long long total = (long long)sk_tiles * ktiles;
         auto start = [&](long long w) { return w * total / G; };
         auto owner = [&](long long i) { return ((i + 1) * G + total - 1) / total - 1; };
         const int w = xcd_logical();
@@ -679,6 +687,19 @@ void sgemm_mfma32(GemmArgs g) {
             tile_of(t, g.tiles_m, g.tiles_n, tm, tn);
             run_tile(tm, tn, kb, ke, sg);
             it += ke - kb;
+        }
+        // Whole tiles, one per workgroup per wave: the workgroups of a wave
+        // sweep k together, so the A and B panels they share stay in L2.
+        for (int t = sk_tiles + w; t < tiles; t += (int)G) {
+            SegInfo sg;
+            sg.counter = t;
+            sg.nseg = 1;
+            sg.seg = 0;
+            sg.s0 = sg.sbase = 0;
+            sg.sstep = 2;
+            int tm, tn;
+            tile_of(t, g.tiles_m, g.tiles_n, tm, tn);
+            run_tile(tm, tn, 0, ktiles, sg);
         }
     } else {
         int tm, tn, split;
@@ -1086,7 +1107,7 @@ __global__ __launch_bounds__((64 * band_waves<MB, FAST>())) void sgemm_skinny_ba
         return;
     }
 
-    // Partials are written and read with system-scope relaxed atomics, i.e.
+    // Partials are written and read with device-scope relaxed atomics, i.e.
     // stores written through to, and loads served from, the point where all
     // XCDs are coherent; each thread's stores have completed (s_waitcnt 0)
     // before the barrier that precedes the counter increment, and the last
@@ -1097,12 +1118,12 @@ __global__ __launch_bounds__((64 * band_waves<MB, FAST>())) void sgemm_skinny_ba
         float sum = 0.0f;
 #pragma unroll
         for (int v = 0; v < W; ++v) sum += red[v][idx];
-        __hip_atomic_store(part + idx, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(part + idx, sum, __ATOMIC_RELAXED, kExchangeScope);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-        is_last = __hip_atomic_fetch_add(&sa.counters[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == S - 1;
+        is_last = __hip_atomic_fetch_add(&sa.counters[tile], 1, __ATOMIC_RELAXED, kExchangeScope) == S - 1;
     __syncthreads();
     if (!is_last) return;
     // The loads of eight splits are issued before they are summed; the sum
@@ -1118,7 +1139,7 @@ __global__ __launch_bounds__((64 * band_waves<MB, FAST>())) void sgemm_skinny_ba
             float v[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                v[i] = sp0 + i < S ? __hip_atomic_load(p + (size_t)i * T, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                v[i] = sp0 + i < S ? __hip_atomic_load(p + (size_t)i * T, __ATOMIC_RELAXED, kExchangeScope)
                                    : 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -1126,7 +1147,7 @@ __global__ __launch_bounds__((64 * band_waves<MB, FAST>())) void sgemm_skinny_ba
         }
         finish(i, idx, sum);
     }
-    if (tid == 0) __hip_atomic_store(&sa.counters[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (tid == 0) __hip_atomic_store(&sa.counters[tile], 0, __ATOMIC_RELAXED, kExchangeScope);
 }
 
 __global__ __launch_bounds__(256) void zero_ints(int *p, int n) {
@@ -1443,6 +1464,7 @@ hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int spl
     const int ktiles = (g.K + CFG::BK - 1) / CFG::BK;
     g.splits = 1;
     g.kt_per_split = ktiles;
+    g.sk_dp_tiles = 0;
     g.ws = nullptr;
     g.counters = nullptr;
     if (CFG::SPLIT && split_slots > 0) {
@@ -1490,6 +1512,13 @@ hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int spl
             }
         }
         workgroups = (unsigned)G;
+        // All but the last full wave of tiles go data-parallel, so that only
+        // one to two waves' worth is shared out (see sgemm_mfma32): shares
+        // that start at different k offsets share no A or B panels in L2, and
+        // over several waves that costs more than the balance gains (5000^3:
+        // 113 TFLOP/s all stream-K, 125 with this split).
+        const long long waves = tiles / G;
+        g.sk_dp_tiles = (int)(waves > 1 ? (waves - 1) * G : 0);
     }
     if (!ta && !tb) return launch_t<CFG, false, false>(g, workgroups, stream);
     if (!ta && tb) return launch_t<CFG, false, true>(g, workgroups, stream);
@@ -1531,6 +1560,7 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     g.beta = beta;
     g.splits = 1;
     g.kt_per_split = 0;
+    g.sk_dp_tiles = 0;
     g.ws = nullptr;
     g.counters = nullptr;
     g.vec_ab = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;

@@ -245,7 +245,8 @@ SPLIT_TILE = [i for i, n in enumerate(_NAMES) if n.startswith("mfma32_") and n.e
 @pytest.mark.parametrize("M,N,K", [(256, 256, 4096),    # 4 tiles, each cut across dozens of workgroups
                                    (1000, 1300, 700),   # ragged edges, tiles cut mid-k
                                    (129, 1000, 3001),   # ragged k tail inside a cut tile
-                                   (2304, 2304, 96)])   # many tiles, three k-tiles each
+                                   (2304, 2304, 96),    # many tiles, three k-tiles each
+                                   (5000, 4100, 96)])   # > 2 waves of tiles: whole-tile waves after the shares
 def test_split_and_stream_k_integer(config, ta, tb, M, N, K):
     """Tiles whose k-range is cut between workgroups: integer inputs, so the
     result is bit-exact whatever the cut and the partial-sum order."""
