@@ -19,7 +19,7 @@ __all__ = [
     "MisgemmError", "library_path", "load_library",
     "mi_sgemm", "mi_sgemm_with_config", "mi_sgemm_select_config",
     "mi_sgemm_config_count", "mi_sgemm_config_name", "mi_sgemm_status_string",
-    "sgemm", "config_names",
+    "mi_sgemm_release_workspace", "sgemm", "config_names",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -57,6 +57,8 @@ def load_library():
     lib.mi_sgemm_config_name.restype = ctypes.c_char_p
     lib.mi_sgemm_status_string.argtypes = [i]
     lib.mi_sgemm_status_string.restype = ctypes.c_char_p
+    lib.mi_sgemm_release_workspace.argtypes = [p]
+    lib.mi_sgemm_release_workspace.restype = i
     _lib = lib
     return lib
 
@@ -99,6 +101,11 @@ def mi_sgemm_config_name(config) -> str | None:
 
 def mi_sgemm_status_string(status) -> str:
     return load_library().mi_sgemm_status_string(int(status)).decode()
+
+
+def mi_sgemm_release_workspace(stream=0) -> int:
+    """C ABI mi_sgemm_release_workspace (integer stream handle); returns the status code."""
+    return load_library().mi_sgemm_release_workspace(stream or None)
 
 
 def config_names() -> list[str]:

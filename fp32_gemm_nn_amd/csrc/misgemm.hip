@@ -1621,6 +1621,19 @@ extern "C" int mi_sgemm_select_config(char transA, char transB, int M, int N, in
     return select_config(transA, transB, M, N, K);
 }
 
+extern "C" int mi_sgemm_release_workspace(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MISGEMM_LAUNCH_FAILED;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto it = g_ws.find(std::make_pair(dev, stream));
+    if (it == g_ws.end()) return MISGEMM_SUCCESS;
+    if (hipStreamSynchronize(stream) != hipSuccess) return MISGEMM_LAUNCH_FAILED;
+    const hipError_t e1 = hipFree(it->second.partials);
+    const hipError_t e2 = hipFree(it->second.counters);
+    g_ws.erase(it);
+    return (e1 == hipSuccess && e2 == hipSuccess) ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
+}
+
 extern "C" int mi_sgemm_config_count(void) { return kNumConfigs; }
 
 extern "C" const char *mi_sgemm_config_name(int config) {

@@ -11,7 +11,9 @@
  * (v_mfma_f32_32x32x2_f32 / v_mfma_f32_16x16x4_f32): FP32 inputs, FP32
  * products and FP32 accumulation, with no reduced-precision emulation.
  *
- * Threading: every entry point is thread-safe and keeps no mutable state.
+ * Threading: every entry point is thread-safe. The only mutable state is the
+ * set of split-K workspaces (one per device and stream, see mi_sgemm), which
+ * a lock guards.
  */
 #ifndef MISGEMM_H
 #define MISGEMM_H
@@ -62,9 +64,15 @@ extern "C" {
  * carried in FP32 in a fixed order, so repeated calls give identical bits.
  *
  * Ownership: all three matrices are device memory owned by the caller. The
- * call allocates and frees nothing, does not synchronise, and returns once
- * the kernels are enqueued; the caller synchronises `stream` before reading
- * C. C must not overlap A or B.
+ * call does not synchronise and returns once the kernels are enqueued; the
+ * caller synchronises `stream` before reading C. C must not overlap A or B.
+ * The first call on a (device, stream) whose kernel splits the k range over
+ * workgroups (split-K or stream-K) allocates that stream's workspace: 64 MiB
+ * of partial blocks and 256 KiB of counters, kept until
+ * mi_sgemm_release_workspace or the end of the process. Calls on one stream
+ * use its workspace in stream order; calls on different streams never share
+ * one. If it cannot be allocated the kernel runs unsplit. No other call
+ * allocates or frees memory.
  *
  * Alignment: any pointer and leading dimension is accepted. 16-byte aligned
  * pointers with lda, ldb, ldc multiples of 4 take the dwordx4 path.
@@ -107,6 +115,17 @@ const char *mi_sgemm_config_name(int config);
 
 /* Static description of a status code (never NULL; owned by the library). */
 const char *mi_sgemm_status_string(int status);
+
+/*
+ * mi_sgemm_release_workspace: free the split-K workspace kept for `stream` on
+ * the current device, if any, after waiting for the work already enqueued on
+ * that stream (hipStreamSynchronize). Meant for callers that destroy streams
+ * which ran split products: call it before hipStreamDestroy to return the
+ * memory. A later split call on the stream allocates a fresh workspace.
+ * Returns MISGEMM_SUCCESS (also when there was none), or
+ * MISGEMM_LAUNCH_FAILED if waiting for the stream or freeing failed.
+ */
+int mi_sgemm_release_workspace(hipStream_t stream);
 
 #ifdef __cplusplus
 }

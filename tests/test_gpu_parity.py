@@ -282,6 +282,28 @@ def test_stream_k_deterministic_and_concurrent(config):
     assert all(np.array_equal(C.cpu().numpy().view(np.uint32), ref.view(np.uint32)) for C in outs)
 
 
+@pytest.mark.parametrize("which", ["band", "streamk"])
+def test_release_workspace_then_split_again(which):
+    """mi_sgemm_release_workspace waits for the stream and frees its workspace;
+    the next split call on that stream allocates a fresh one and is correct."""
+    if which == "band":
+        case, config = W.C5B.with_(beta=0.0), BAND
+    else:
+        case, config = W.C1, STREAMK[0]
+    inp = W.make_inputs(case)
+    want = run_oracle(case, inp)
+    A = torch.from_numpy(inp.A).cuda()
+    B = torch.from_numpy(inp.B).cuda()
+    st = torch.cuda.Stream()
+    for rep in range(3):
+        with torch.cuda.stream(st):
+            C = torch.full((case.M, case.N), float("nan"), device="cuda")
+        mg.sgemm(case.transA, case.transB, case.alpha, A, B, 0.0, C, stream=st.cuda_stream, config=config)
+        assert mg.mi_sgemm_release_workspace(st.cuda_stream) == 0
+        compare(case, C.cpu().numpy(), want, False)
+    assert mg.mi_sgemm_release_workspace(torch.cuda.Stream().cuda_stream) == 0   # none kept: no-op
+
+
 # --- every kernel configuration on ragged shapes ------------------------------------------
 
 def _edge_triples(count, seed):
@@ -335,6 +357,39 @@ def test_large_tile_path_with_padding():
     inp = W.make_inputs(case)
     got = run_gpu(case, inp, lda=260, ldb=2052, ldc=2056)
     compare(case, got, run_oracle(case, inp), True)
+
+
+# --- IEEE special values ------------------------------------------------------------------
+
+@pytest.mark.parametrize("config", range(NCONFIG))
+@pytest.mark.parametrize("ta,tb", OPS)
+def test_special_values_propagate(config, ta, tb):
+    """+Inf in one entry of op(A) and NaN in one entry of op(B): the outputs
+    they reach are +-Inf or NaN exactly where IEEE arithmetic puts them (the
+    integer fill has zeros, so Inf * 0 = NaN occurs), and every other output
+    is bit-exact."""
+    M, N, K = 150, 230, 97
+    i0, k0, k1, j1 = 77, 40, 61, 129
+    case = W.Case(f"special_{ta}{tb}_cfg{config}", ta, tb, M, N, K, 1.0, -1.0, seed=90, fill="int_rand")
+    note(case.name)
+    inp = W.make_inputs(case)
+    if ta == "N":
+        inp.A[i0, k0] = np.inf
+    else:
+        inp.A[k0, i0] = np.inf
+    if tb == "N":
+        inp.B[k1, j1] = np.nan
+    else:
+        inp.B[j1, k1] = np.nan
+    got = run_gpu(case, inp, config=config)
+    want = run_oracle(case, inp)
+    assert np.isnan(want[:, j1]).all() and np.isinf(want[i0]).any()
+    assert np.array_equal(np.isnan(got), np.isnan(want)), f"{case.name}: NaN positions differ"
+    inf = np.isinf(want)
+    assert np.array_equal(np.isinf(got), inf), f"{case.name}: Inf positions differ"
+    assert np.array_equal(np.signbit(got[inf]), np.signbit(want[inf])), f"{case.name}: Inf signs differ"
+    fin = np.isfinite(want)
+    assert np.array_equal(got[fin], want[fin]), f"{case.name}: finite outputs differ"
 
 
 # --- BLAS semantics of the scalars and empty sizes ------------------------------------------
