@@ -38,8 +38,22 @@
 //   * Workgroup order: consecutive workgroups are dealt round-robin to the 8
 //     XCDs, each with its own L2. The launch index is remapped so each XCD
 //     receives one contiguous run of tiles, walked in column groups of
-//     GROUP_M tile rows, so tiles sharing A rows and B columns meet in the
+//     kGroupM tile rows, so tiles sharing A rows and B columns meet in the
 //     same L2.
+//
+// Ways of dividing the k range (compile-time per configuration):
+//   * k-groups (KG > 1): KG groups of waves in one workgroup take alternate
+//     k-tiles, each with its own LDS buffers, and are summed through LDS in
+//     group order.
+//   * Split-K over workgroups (SPLIT): S workgroups share one tile's k range;
+//     each stores its partial tile, and the last to finish sums the S
+//     partials in split order (see sgemm_mfma32).
+//   * Stream-K (STREAMK): one or two workgroups per CU each take an equal
+//     share of all (tile, k-tile) iterations, with the same exchange for the
+//     tiles cut between workgroups; all but the last wave of tiles run whole.
+// No workgroup ever waits for another, and every sum has a fixed order, so
+// repeated calls give identical bits. The skinny kernels (M <= 32, bound by
+// HBM) are described with their code.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1180,7 +1194,7 @@ using CfgT = TileCfg<128, 256, 32, 2, 4>;        // 8 waves, 64 x 64 per wave
 using CfgT16 = TileCfg<128, 256, 16, 2, 2>;      // 4 waves, 64 x 128 per wave, 2 per CU
 using CfgQ32 = TileCfg<256, 256, 32, 4, 2>;      // 8 waves, 64 x 128 per wave, 1 per CU
 // Split-K over workgroups (for grids with fewer tiles than CU slots).
-using CfgL42K = TileCfg<128, 128, 32, 4, 2, 1, 0, true>;
+using CfgL42K = TileCfg<128, 128, 32, 4, 2, 1, 0, true>;   // one per CU
 using CfgSK = TileCfg<64, 64, 32, 2, 2, 1, 0, true>;
 using CfgLK = TileCfg<128, 128, 32, 2, 2, 1, 0, true>;
 // Stream-K: one workgroup per CU (two waves per SIMD), or two (four).
@@ -1188,6 +1202,30 @@ using CfgL42S1 = TileCfg<128, 128, 32, 4, 2, 1, 2, false, true>;
 using CfgL42S2 = TileCfg<128, 128, 32, 4, 2, 1, 4, false, true>;
 using CfgWS = TileCfg<256, 128, 32, 4, 2, 1, 0, false, true>;   // one workgroup per CU
 using CfgTS = TileCfg<128, 256, 32, 2, 4, 1, 0, false, true>;
+
+// Config ids: the index of each entry of kConfigs below.
+enum ConfigId : int {
+    kCfg128 = 0,
+    kCfg64 = 1,
+    kCfgSkinny16 = 2,
+    kCfgBand = 3,
+    kCfg64Kg2 = 4,
+    kCfg64Kg4 = 5,
+    kCfg128Kg2 = 6,
+    kCfg128W24 = 7,
+    kCfg128W42 = 8,
+    kCfg256x128 = 9,
+    kCfg128x256 = 10,
+    kCfg128W42Split = 11,
+    kCfg64Split = 12,
+    kCfg128Split = 13,
+    kCfg128x256x16 = 14,
+    kCfg256x256 = 15,
+    kCfgStreamK1 = 16,
+    kCfgStreamK2 = 17,
+    kCfgStreamK256x128 = 18,
+    kCfgStreamK128x256 = 19,
+};
 
 struct ConfigInfo {
     const char *name;
@@ -1216,10 +1254,27 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_256x128x32_w4x2_streamk", CfgWS::BM, CfgWS::BN, CfgWS::NT},
     {"mfma32_128x256x32_w2x4_streamk", CfgTS::BM, CfgTS::BN, CfgTS::NT},
 };
-constexpr int kSkinnyConfig = 2;
-constexpr int kBandConfig = 3;
 constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+static_assert(kNumConfigs == kCfgStreamK128x256 + 1, "one ConfigId per kConfigs entry");
+static_assert(kConfigs[kCfg128].bm == CfgL::BM && kConfigs[kCfg128].bn == CfgL::BN && kConfigs[kCfg128].nt == CfgL::NT, "kConfigs order");
+static_assert(kConfigs[kCfg64].bm == CfgS::BM && kConfigs[kCfg64].bn == CfgS::BN && kConfigs[kCfg64].nt == CfgS::NT, "kConfigs order");
+static_assert(kConfigs[kCfg64Kg2].bm == CfgS2::BM && kConfigs[kCfg64Kg2].bn == CfgS2::BN && kConfigs[kCfg64Kg2].nt == CfgS2::NT, "kConfigs order");
+static_assert(kConfigs[kCfg64Kg4].bm == CfgS4::BM && kConfigs[kCfg64Kg4].bn == CfgS4::BN && kConfigs[kCfg64Kg4].nt == CfgS4::NT, "kConfigs order");
+static_assert(kConfigs[kCfg128Kg2].bm == CfgL2::BM && kConfigs[kCfg128Kg2].bn == CfgL2::BN && kConfigs[kCfg128Kg2].nt == CfgL2::NT, "kConfigs order");
+static_assert(kConfigs[kCfg128W24].bm == CfgL24::BM && kConfigs[kCfg128W24].bn == CfgL24::BN && kConfigs[kCfg128W24].nt == CfgL24::NT, "kConfigs order");
+static_assert(kConfigs[kCfg128W42].bm == CfgL42::BM && kConfigs[kCfg128W42].bn == CfgL42::BN && kConfigs[kCfg128W42].nt == CfgL42::NT, "kConfigs order");
+static_assert(kConfigs[kCfg256x128].bm == CfgW::BM && kConfigs[kCfg256x128].bn == CfgW::BN && kConfigs[kCfg256x128].nt == CfgW::NT, "kConfigs order");
+static_assert(kConfigs[kCfg128x256].bm == CfgT::BM && kConfigs[kCfg128x256].bn == CfgT::BN && kConfigs[kCfg128x256].nt == CfgT::NT, "kConfigs order");
+static_assert(kConfigs[kCfg128W42Split].bm == CfgL42K::BM && kConfigs[kCfg128W42Split].bn == CfgL42K::BN && kConfigs[kCfg128W42Split].nt == CfgL42K::NT, "kConfigs order");
+static_assert(kConfigs[kCfg64Split].bm == CfgSK::BM && kConfigs[kCfg64Split].bn == CfgSK::BN && kConfigs[kCfg64Split].nt == CfgSK::NT, "kConfigs order");
+static_assert(kConfigs[kCfg128Split].bm == CfgLK::BM && kConfigs[kCfg128Split].bn == CfgLK::BN && kConfigs[kCfg128Split].nt == CfgLK::NT, "kConfigs order");
+static_assert(kConfigs[kCfg128x256x16].bm == CfgT16::BM && kConfigs[kCfg128x256x16].bn == CfgT16::BN && kConfigs[kCfg128x256x16].nt == CfgT16::NT, "kConfigs order");
+static_assert(kConfigs[kCfg256x256].bm == CfgQ32::BM && kConfigs[kCfg256x256].bn == CfgQ32::BN && kConfigs[kCfg256x256].nt == CfgQ32::NT, "kConfigs order");
+static_assert(kConfigs[kCfgStreamK1].bm == CfgL42S1::BM && kConfigs[kCfgStreamK1].bn == CfgL42S1::BN && kConfigs[kCfgStreamK1].nt == CfgL42S1::NT, "kConfigs order");
+static_assert(kConfigs[kCfgStreamK2].bm == CfgL42S2::BM && kConfigs[kCfgStreamK2].bn == CfgL42S2::BN && kConfigs[kCfgStreamK2].nt == CfgL42S2::NT, "kConfigs order");
+static_assert(kConfigs[kCfgStreamK256x128].bm == CfgWS::BM && kConfigs[kCfgStreamK256x128].bn == CfgWS::BN && kConfigs[kCfgStreamK256x128].nt == CfgWS::NT, "kConfigs order");
+static_assert(kConfigs[kCfgStreamK128x256].bm == CfgTS::BM && kConfigs[kCfgStreamK128x256].bn == CfgTS::BN && kConfigs[kCfgStreamK128x256].nt == CfgTS::NT, "kConfigs order");
 constexpr int kNumCus = 256;
 
 bool op_n(char t) { return t == 'N' || t == 'n'; }
@@ -1283,7 +1338,7 @@ double cu_balance(long long tiles, int slots = 1) {
 int select_config(char transA, char transB, int M, int N, int K) {
     (void)transA;
     (void)K;
-    if (M <= kSkinnyMaxM) return kBandConfig;
+    if (M <= kSkinnyMaxM) return kCfgBand;
     auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const long long t128 = tiles(128, 128), t64 = tiles(64, 64);
     // Stream-K work: 128 x 128 x 32 iterations.
@@ -1301,25 +1356,25 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const double s_skb = (sk_ok && !tb) ? 0.955 : -1.0;
         const double s_sk = sk_ok ? 0.925 : -1.0;
         const double best = fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(s_128, s_64));
-        if (best == s_q) return 15;
-        if (best == s_skb) return tall ? 18 : 19;
-        if (best == s_sk) return 17;
-        if (best == s_b4) return 14;
-        if (best == s_b8) return tall ? 9 : 10;
-        return best == s_128 ? 8 : 1;
+        if (best == s_q) return kCfg256x256;
+        if (best == s_skb) return tall ? kCfgStreamK256x128 : kCfgStreamK128x256;
+        if (best == s_sk) return kCfgStreamK2;
+        if (best == s_b4) return kCfg128x256x16;
+        if (best == s_b8) return tall ? kCfg256x128 : kCfg128x256;
+        return best == s_128 ? kCfg128W42 : kCfg64;
     }
     // 144..255 tiles of 128 x 128 with at least 20 k-tiles per workgroup:
     // stream-K, one workgroup per CU.
-    if (t128 >= 144 && sk_iters >= 20LL * kNumCus) return 16;
-    if (t128 >= 3 * kNumCus / 4) return 8;
-    if (t64 >= 2 * kNumCus) return 1;
+    if (t128 >= 144 && sk_iters >= 20LL * kNumCus) return kCfgStreamK1;
+    if (t128 >= 3 * kNumCus / 4) return kCfg128W42;
+    if (t64 >= 2 * kNumCus) return kCfg64;
     // 257..511 tiles of 64 x 64: two k-groups unless their workgroups would
     // leave the CU slots badly filled; then split-K over workgroups, whose
     // smaller workgroups spread more evenly.
-    if (t64 > kNumCus) return (double)t64 / (2 * kNumCus) >= 0.7 ? 4 : 12;
+    if (t64 > kNumCus) return (double)t64 / (2 * kNumCus) >= 0.7 ? kCfg64Kg2 : kCfg64Split;
     // Up to 96 tiles of 64 x 64 (n <= ~600): split-K over workgroups.
-    if (t64 <= 96) return 12;
-    return 5;
+    if (t64 <= 96) return kCfg64Split;
+    return kCfg64Kg4;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1567,30 +1622,30 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     g.vec_c = aligned16(C) && ldc % 4 == 0;
     const bool ta = op_t(transA), tb = op_t(transB);
     if (config < 0) config = select_config(transA, transB, M, N, K);
-    if ((config == kSkinnyConfig || config == kBandConfig) && (M + 2 * 16 - 1) / (2 * 16) > 65535)
+    if ((config == kCfgSkinny16 || config == kCfgBand) && (M + 2 * 16 - 1) / (2 * 16) > 65535)
         return MISGEMM_TOO_LARGE;
     hipError_t err;
     switch (config) {
-        case 0: err = launch_cfg<CfgL>(ta, tb, g, stream); break;
-        case 1: err = launch_cfg<CfgS>(ta, tb, g, stream); break;
-        case kSkinnyConfig: err = launch_skinny(ta, tb, g, stream); break;
-        case kBandConfig: err = launch_band(ta, tb, g, stream); break;
-        case 4: err = launch_cfg<CfgS2>(ta, tb, g, stream); break;
-        case 5: err = launch_cfg<CfgS4>(ta, tb, g, stream); break;
-        case 6: err = launch_cfg<CfgL2>(ta, tb, g, stream); break;
-        case 7: err = launch_cfg<CfgL24>(ta, tb, g, stream); break;
-        case 8: err = launch_cfg<CfgL42>(ta, tb, g, stream); break;
-        case 9: err = launch_cfg<CfgW>(ta, tb, g, stream); break;
-        case 10: err = launch_cfg<CfgT>(ta, tb, g, stream); break;
-        case 11: err = launch_cfg<CfgL42K>(ta, tb, g, stream, 1); break;
-        case 12: err = launch_cfg<CfgSK>(ta, tb, g, stream, 2); break;
-        case 13: err = launch_cfg<CfgLK>(ta, tb, g, stream, 1); break;
-        case 14: err = launch_cfg<CfgT16>(ta, tb, g, stream); break;
-        case 15: err = launch_cfg<CfgQ32>(ta, tb, g, stream); break;
-        case 16: err = launch_cfg<CfgL42S1>(ta, tb, g, stream); break;
-        case 17: err = launch_cfg<CfgL42S2>(ta, tb, g, stream); break;
-        case 18: err = launch_cfg<CfgWS>(ta, tb, g, stream); break;
-        default: err = launch_cfg<CfgTS>(ta, tb, g, stream); break;
+        case kCfg128: err = launch_cfg<CfgL>(ta, tb, g, stream); break;
+        case kCfg64: err = launch_cfg<CfgS>(ta, tb, g, stream); break;
+        case kCfgSkinny16: err = launch_skinny(ta, tb, g, stream); break;
+        case kCfgBand: err = launch_band(ta, tb, g, stream); break;
+        case kCfg64Kg2: err = launch_cfg<CfgS2>(ta, tb, g, stream); break;
+        case kCfg64Kg4: err = launch_cfg<CfgS4>(ta, tb, g, stream); break;
+        case kCfg128Kg2: err = launch_cfg<CfgL2>(ta, tb, g, stream); break;
+        case kCfg128W24: err = launch_cfg<CfgL24>(ta, tb, g, stream); break;
+        case kCfg128W42: err = launch_cfg<CfgL42>(ta, tb, g, stream); break;
+        case kCfg256x128: err = launch_cfg<CfgW>(ta, tb, g, stream); break;
+        case kCfg128x256: err = launch_cfg<CfgT>(ta, tb, g, stream); break;
+        case kCfg128W42Split: err = launch_cfg<CfgL42K>(ta, tb, g, stream, 1); break;
+        case kCfg64Split: err = launch_cfg<CfgSK>(ta, tb, g, stream, 2); break;
+        case kCfg128Split: err = launch_cfg<CfgLK>(ta, tb, g, stream, 1); break;
+        case kCfg128x256x16: err = launch_cfg<CfgT16>(ta, tb, g, stream); break;
+        case kCfg256x256: err = launch_cfg<CfgQ32>(ta, tb, g, stream); break;
+        case kCfgStreamK1: err = launch_cfg<CfgL42S1>(ta, tb, g, stream); break;
+        case kCfgStreamK2: err = launch_cfg<CfgL42S2>(ta, tb, g, stream); break;
+        case kCfgStreamK256x128: err = launch_cfg<CfgWS>(ta, tb, g, stream); break;
+        default: err = launch_cfg<CfgTS>(ta, tb, g, stream); break;   // kCfgStreamK128x256
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }
