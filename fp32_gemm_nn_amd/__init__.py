@@ -42,6 +42,11 @@ def load_library():
         raise RuntimeError(
             f"HIP library not built: {library_path} is missing. "
             "Run `python -m fp32_gemm_nn_amd.build` (or __graft_entry__.build()).")
+    # torch ships its own HIP runtime (libamdhip64.so.7 under torch/lib). Load
+    # it first, so that this library's libamdhip64.so.7 resolves to the same
+    # copy: loaded the other way round, the process ends up with two HIP and
+    # two HSA runtimes, and the one this library uses finds no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(library_path)
     c, i, f, p = ctypes.c_char, ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     gemm_args = [c, c, i, i, i, f, p, i, p, i, f, p, i, p]

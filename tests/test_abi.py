@@ -156,3 +156,19 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mg, "library_path", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         mg.mi_sgemm_config_count()
+
+
+def test_one_hip_runtime_when_library_is_loaded_first():
+    """Using the library before torch must not load a second HIP runtime: the
+    binding loads torch's copy first, and libmisgemm.so binds to that one."""
+    import subprocess
+    import sys
+    code = ("import fp32_gemm_nn_amd as mg\n"
+            "mg.config_names()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = {l.split()[-1] for l in maps if 'libamdhip64' in l or 'libhsa-runtime64' in l}\n"
+            "print(len([l for l in libs if 'libamdhip64' in l]), len([l for l in libs if 'libhsa-runtime64' in l]))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["1", "1"], out.stdout
