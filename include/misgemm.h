@@ -123,7 +123,8 @@ const char *mi_sgemm_status_string(int status);
  * which ran split products: call it before hipStreamDestroy to return the
  * memory. A later split call on the stream allocates a fresh workspace.
  * Returns MISGEMM_SUCCESS (also when there was none), or
- * MISGEMM_LAUNCH_FAILED if waiting for the stream or freeing failed.
+ * MISGEMM_LAUNCH_FAILED if waiting for the stream or freeing failed. It must
+ * not run while another thread enqueues an mi_sgemm call on the same stream.
  */
 int mi_sgemm_release_workspace(hipStream_t stream);
 
