@@ -1336,31 +1336,35 @@ double cu_balance(long long tiles, int slots = 1) {
 //                       the CU slots; <= 96 split-K over workgroups; else
 //                       four k-groups.
 int select_config(char transA, char transB, int M, int N, int K) {
-    (void)transA;
-    (void)K;
     if (M <= kSkinnyMaxM) return kCfgBand;
     auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const long long t128 = tiles(128, 128), t64 = tiles(64, 64);
     // Stream-K work: 128 x 128 x 32 iterations.
     const long long sk_iters = t128 * ((K + 31) / 32);
     if (t128 >= kNumCus) {
-        const bool tb = op_t(transB);
-        const bool tall = M >= N;
-        const double s_q = tb ? -1.0 : 1.044 * cu_balance(tiles(256, 256));
-        const double s_b4 = tb ? -1.0 : 1.038 * cu_balance(tiles(128, 256), 2);
-        const double s_b8 = tb ? -1.0 : 1.024 * cu_balance(tall ? tiles(256, 128) : tiles(128, 256));
+        const bool ta = op_t(transA), tb = op_t(transB);
+        // Big tiles (one workgroup per CU) lose to 128 x 128 (two per CU)
+        // when K is short and the grid fills the chip only once, except with
+        // only A transposed; with both transposed, 256 x 128 is the one that
+        // gains (the 256 x 256 and 128 x 256 x 16 tiles do not).
+        const bool big_ok = !(K < 2048 && t128 < 4 * kNumCus) || (ta && !tb);
+        const bool tt = ta && tb;
+        const bool wide = !tt && M < N;    // 128 x 256 rather than 256 x 128
+        const double s_q = big_ok ? (tt ? 1.0 : 1.044) * cu_balance(tiles(256, 256)) : -1.0;
+        const double s_b4 = big_ok ? (tt ? 1.0 : 1.038) * cu_balance(tiles(128, 256), 2) : -1.0;
+        const double s_b8 = big_ok ? (tt ? 1.034 : 1.024) * cu_balance(wide ? tiles(128, 256) : tiles(256, 128)) : -1.0;
         const double s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
         // Stream-K fills every CU slot whatever the tile count: with the
-        // 256 x 128 / 128 x 256 tile (B not transposed), else 128 x 128.
+        // 256 x 128 / 128 x 256 tile where big tiles pay, else 128 x 128.
         const bool sk_ok = sk_iters >= 8LL * 2 * kNumCus;
-        const double s_skb = (sk_ok && !tb) ? 0.955 : -1.0;
+        const double s_skb = (sk_ok && big_ok) ? 0.955 : -1.0;
         const double s_sk = sk_ok ? 0.925 : -1.0;
         const double best = fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(s_128, s_64));
         if (best == s_q) return kCfg256x256;
-        if (best == s_skb) return tall ? kCfgStreamK256x128 : kCfgStreamK128x256;
+        if (best == s_skb) return wide ? kCfgStreamK128x256 : kCfgStreamK256x128;
         if (best == s_sk) return kCfgStreamK2;
         if (best == s_b4) return kCfg128x256x16;
-        if (best == s_b8) return tall ? kCfg256x128 : kCfg128x256;
+        if (best == s_b8) return wide ? kCfg128x256 : kCfg256x128;
         return best == s_128 ? kCfg128W42 : kCfg64;
     }
     // 144..255 tiles of 128 x 128 with at least 20 k-tiles per workgroup:

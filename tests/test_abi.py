@@ -112,12 +112,15 @@ def test_shape_class_selection():
     # 4096^2 output: 256 tiles of 256 x 256, one per CU.
     assert sel("N", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
     assert sel("T", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
-    # B transposed: no big tiles; 128 x 128 with 8 waves.
-    assert sel("N", "T", 4096, 4096, 4096) == "mfma32_128x128x32_w4x2"
-    # 2048 x 4096: 256 such tiles only (one per CU): the 8-wave big tile,
-    # unless B is transposed.
-    assert sel("N", "N", 2048, 4096, 1024) == "mfma32_128x256x32_w2x4"
+    # Both transposed: 256 x 128 is the big tile that pays.
+    assert sel("N", "T", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
+    assert sel("T", "T", 4096, 4096, 4096) == "mfma32_256x128x32_w4x2"
+    assert sel("T", "T", 2048, 4096, 2048) == "mfma32_256x128x32_w4x2"
+    # 2048 x 4096 x 1024: short K on a grid that fills the chip once: 128 x 128
+    # (two workgroups per CU), except with only A transposed.
+    assert sel("N", "N", 2048, 4096, 1024) == "mfma32_128x128x32_w4x2"
     assert sel("T", "N", 2048, 4096, 1024) == "mfma32_128x256x32_w2x4"
+    assert sel("N", "N", 2048, 4096, 2048) == "mfma32_128x256x32_w2x4"
     assert sel("T", "T", 2048, 4096, 1024) == "mfma32_128x128x32_w4x2"
     assert sel("N", "T", 2048, 4096, 1024) == "mfma32_128x128x32_w4x2"
     # 1024^2 output: 64 tiles of 128 x 128 only, so smaller tiles with four k-groups.
@@ -138,9 +141,11 @@ def test_shape_class_selection():
                     (3328, skw), (3584, skw), (3840, skw), (4096, "256x256x32_w4x2"),
                     (8192, "256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == "mfma32_" + want, n
-    # B transposed: no big tiles, so stream-K runs 128 x 128 tiles, two per CU.
-    assert sel("N", "T", 3072, 3072, 3072) == "mfma32_128x128x32_w4x2_streamk_2wg"
-    assert sel("T", "T", 2560, 2560, 2560) == "mfma32_128x128x32_w4x2_streamk_2wg"
+    # Stream-K over big tiles for the transposed op pairs too; 128 x 128 (two
+    # per CU) where big tiles do not pay.
+    assert sel("N", "T", 3072, 3072, 3072) == "mfma32_256x128x32_w4x2_streamk"
+    assert sel("T", "T", 2560, 2560, 2560) == "mfma32_256x128x32_w4x2_streamk"
+    assert sel("N", "T", 2304, 2304, 1024) == "mfma32_128x128x32_w4x2_streamk_2wg"
     # N > M: the 128 x 256 stream-K tile.
     assert sel("N", "N", 2304, 3328, 2048) == "mfma32_128x256x32_w2x4_streamk"
     # M <= 32: the skinny, bandwidth-bound kernel.
