@@ -73,6 +73,7 @@ class Problem:
 
         self.case = case
         inp = W.make_inputs(case)
+        self.inp = inp                      # host copy (the oracle's input)
         self.sets = []
         for i in range(copies):
             A = torch.from_numpy(inp.A).cuda()
@@ -112,6 +113,38 @@ def time_problem(prob, steps, warmup, config=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, ev0.elapsed_time(ev1) / 1e3
+
+
+def per_call_stats(prob, calls, config=None):
+    """Median, minimum and 90th percentile of `calls` single-call HIP-event
+    timings (microseconds), each call bracketed by its own event pair."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        prob.call(i, handle, config)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+    return {"median_us": round(t[len(t) // 2], 3), "min_us": round(t[0], 3), "p90_us": round(t[(len(t) * 9) // 10], 3)}
+
+
+def cpu_baseline_seconds(case, inp):
+    """CPU baseline for one workload: wall time of one product of the CPU
+    oracle, as it stands, on the workload's inputs."""
+    import oracle
+
+    C = inp.C.copy()
+    t0 = time.perf_counter()
+    rc = oracle.sgemm(case.transA, case.transB, case.M, case.N, case.K, case.alpha, inp.A, case.lda_,
+                      inp.B, case.ldb_, case.beta, C, case.ldc_)
+    dt = time.perf_counter() - t0
+    if rc != 0:
+        raise RuntimeError(f"oracle: status {rc}")
+    return dt
 
 
 def cpu_baseline(case, min_seconds=10.0, max_seconds=30.0):
@@ -188,14 +221,18 @@ def run_copy(steps, warmup):
 
 
 def run_table(path, steps, warmup):
-    """Per-workload TFLOPS for every configuration (one JSON object per line)."""
+    """Every workload with the kernel select_config picks for it, one JSON
+    object per line: mean time per call and TFLOP/s; per-call median, minimum
+    and 90th percentile for calls of 20 us or more; for the skinny shapes, HBM
+    rates cold (eight rotating operand sets) and warm (one set); and the CPU
+    baseline (one oracle product) with the GPU's speed-up over it."""
     import fp32_gemm_nn_amd as mg
     from synthetic import workloads as W
 
-    cases = [W.C1, W.C2, *[W.c3(n) for n in W.C3_SIZES], W.C4, *W.C5A, W.C5B]
+    cases = [W.C1, W.C2, *[W.c3(n) for n in W.C3_SIZES], W.C4, *W.C5A, W.C5B, *W.SHARD8]
     with open(path, "w") as out:
         for case in cases:
-            skinny = case is W.C5B
+            skinny = case.M <= 32
             # The skinny product streams 64 MiB of B; rotate 8 independent
             # operand sets (> 512 MiB) so repeated calls do not hit in the
             # 256 MB last-level cache.
@@ -213,6 +250,18 @@ def run_table(path, steps, warmup):
                    "GBps_algorithmic": round(case.algorithmic_bytes / per / 1e9, 1)}
             if skinny:
                 row["pct_hbm_peak"] = round(100 * case.algorithmic_bytes / per / 1e9 / PEAK_HBM_GBPS, 2)
+                # Warm: one operand set, so B stays in the 256 MB last-level cache.
+                warm = Problem(case)
+                _, evw = time_problem(warm, n, warmup)
+                row["us_per_call_warm"] = round(evw / n * 1e6, 3)
+                row["pct_hbm_peak_warm"] = round(100 * case.algorithmic_bytes / (evw / n) / 1e9 / PEAK_HBM_GBPS, 2)
+                del warm
+            if per >= 20e-6:
+                row["per_call"] = per_call_stats(prob, min(n, 200))
+            t_cpu = cpu_baseline_seconds(case, prob.inp)
+            row["cpu_baseline_s"] = round(t_cpu, 4)
+            row["cpu_baseline_gflops"] = round(case.flops / t_cpu / 1e9, 2)
+            row["gpu_speedup_vs_cpu_baseline"] = round(t_cpu / per, 1)
             out.write(json.dumps(row) + "\n")
             out.flush()
             print(json.dumps(row), file=sys.stderr, flush=True)
@@ -224,7 +273,7 @@ def run_workload(name, steps, warmup):
     import fp32_gemm_nn_amd as mg
     from synthetic import workloads as W
 
-    cases = {c.name: c for c in [*W.all_cases(), *[W.c3(n) for n in W.C3_SIZES]]}
+    cases = {c.name: c for c in [*W.all_cases(), *W.SHARD8]}
     if name not in cases:
         raise SystemExit(f"unknown workload {name!r}; one of: {', '.join(sorted(cases))}")
     case = cases[name]

@@ -124,6 +124,11 @@ C5A = tuple(Case(f"{ta}{tb}_2048x4096x1024".lower(), ta, tb, 2048, 4096, 1024, 1
             for ta in "NT" for tb in "NT")
 C5B = Case("nn_skinny_16x4096x4096", "N", "N", 16, 4096, 4096, 1.0, 1.0, seed=5)
 
+# One GPU's share of C4 and C5b split eight ways (rows of C4, columns of C5b):
+# the shard shapes a multi-GPU run would hand each device.
+SHARD8 = (Case("nn_shard8_512x4096x4096", "N", "N", 512, 4096, 4096, 1.0, 0.0, seed=4),
+          Case("nn_skinny_shard8_16x512x4096", "N", "N", 16, 512, 4096, 1.0, 1.0, seed=5))
+
 HEADLINE = C4
 
 

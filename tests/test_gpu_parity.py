@@ -114,7 +114,7 @@ def is_exact(case):
 
 # --- the workload configurations -----------------------------------------------------
 
-CONFIG_CASES = [W.C1, W.C2, W.C2_INT, W.C4, *W.C5A, W.C5B]
+CONFIG_CASES = [W.C1, W.C2, W.C2_INT, W.C4, *W.C5A, W.C5B, *W.SHARD8]
 
 
 @pytest.mark.parametrize("case", CONFIG_CASES, ids=lambda c: c.name)
