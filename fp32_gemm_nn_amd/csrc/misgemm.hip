@@ -1406,13 +1406,38 @@ std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 // Returns nullptr if no workspace can be had (the caller then runs unsplit).
+// The device a stream's work runs on (the current device for the null
+// stream): its workspace lives there, whatever device is current.
+bool stream_device(hipStream_t stream, int &dev) {
+    if (stream == nullptr) return hipGetDevice(&dev) == hipSuccess;
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return false;
+    dev = d;
+    return true;
+}
+
+// Makes `dev` current for its lifetime and restores the caller's device.
+struct DeviceGuard {
+    int saved = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&saved) != hipSuccess) return;
+        ok = saved == dev || hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (saved >= 0) (void)hipSetDevice(saved);
+    }
+};
+
 const Workspace *get_workspace(hipStream_t stream) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    if (!stream_device(stream, dev)) return nullptr;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     auto key = std::make_pair(dev, stream);
     auto it = g_ws.find(key);
     if (it != g_ws.end()) return &it->second;
+    DeviceGuard on_dev(dev);
+    if (!on_dev.ok) return nullptr;
     Workspace w;
     if (hipMalloc(reinterpret_cast<void **>(&w.partials), kWsFloats * sizeof(float)) != hipSuccess) {
         (void)hipGetLastError();
@@ -1682,10 +1707,12 @@ extern "C" int mi_sgemm_select_config(char transA, char transB, int M, int N, in
 
 extern "C" int mi_sgemm_release_workspace(hipStream_t stream) {
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return MISGEMM_LAUNCH_FAILED;
+    if (!stream_device(stream, dev)) return MISGEMM_LAUNCH_FAILED;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     auto it = g_ws.find(std::make_pair(dev, stream));
     if (it == g_ws.end()) return MISGEMM_SUCCESS;
+    DeviceGuard on_dev(dev);
+    if (!on_dev.ok) return MISGEMM_LAUNCH_FAILED;
     if (hipStreamSynchronize(stream) != hipSuccess) return MISGEMM_LAUNCH_FAILED;
     const hipError_t e1 = hipFree(it->second.partials);
     const hipError_t e2 = hipFree(it->second.counters);

@@ -66,8 +66,9 @@ extern "C" {
  * Ownership: all three matrices are device memory owned by the caller. The
  * call does not synchronise and returns once the kernels are enqueued; the
  * caller synchronises `stream` before reading C. C must not overlap A or B.
- * The first call on a (device, stream) whose kernel splits the k range over
- * workgroups (split-K or stream-K) allocates that stream's workspace: 64 MiB
+ * The first call on a stream whose kernel splits the k range over
+ * workgroups (split-K or stream-K) allocates that stream's workspace, on the
+ * stream's device (the current device for the null stream): 64 MiB
  * of partial blocks and 256 KiB of counters, kept until
  * mi_sgemm_release_workspace or the end of the process. Calls on one stream
  * use its workspace in stream order; calls on different streams never share
@@ -117,8 +118,8 @@ const char *mi_sgemm_config_name(int config);
 const char *mi_sgemm_status_string(int status);
 
 /*
- * mi_sgemm_release_workspace: free the split-K workspace kept for `stream` on
- * the current device, if any, after waiting for the work already enqueued on
+ * mi_sgemm_release_workspace: free the split-K workspace kept for `stream`
+ * (on the stream's device; for the null stream, the current device), if any, after waiting for the work already enqueued on
  * that stream (hipStreamSynchronize). Meant for callers that destroy streams
  * which ran split products: call it before hipStreamDestroy to return the
  * memory. A later split call on the stream allocates a fresh workspace.
