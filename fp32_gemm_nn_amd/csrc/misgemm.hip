@@ -1309,6 +1309,47 @@ double cu_balance(long long tiles, int slots = 1) {
     return (double)tiles / (double)(rounds * cap);
 }
 
+// Timing model of the 64 x 64 x 32 tile (four waves; up to four resident per
+// CU, bounded by LDS), in microseconds, for `kgroups` k-groups per workgroup
+// (each a set of four waves) or `splits` workgroups per tile:
+//   T = 4 + kt * max(0.6 u, 0.88) + 2 ceil(S / 4)   (the last term when S > 1)
+// where u = kgroups * ceil(tiles * S / CUs) is the number of four-wave units
+// on the busiest CU and kt the k-tiles each unit runs. A k-tile costs a lone
+// unit 0.88 us (load latency) and 0.6 us per unit once several share the CU;
+// the last workgroup of a split tile sums the partials four at a time, about
+// 2 us per batch. The terms are fitted to timings of every split count and
+// k-group count on square products from 320^3 to 1152^3 and on long-K
+// products (512 x 512 x 4096, 2048 x 256 x 2048) on MI355X; it orders split
+// counts and the split / four-k-group choice correctly up to 256 tiles, but
+// underrates two k-groups above that.
+double model_64x64_us(long long tiles, int ktiles, int kgroups, long long splits) {
+    const long long kt_split = (ktiles + splits - 1) / splits;
+    const long long kt = (kt_split + kgroups - 1) / kgroups;
+    const long long u = kgroups * ((tiles * splits + kNumCus - 1) / kNumCus);
+    double t = 4.0 + (double)kt * std::max(0.6 * (double)u, 0.88);
+    if (splits > 1) t += 2.0 * (double)((splits + 3) / 4);
+    return t;
+}
+
+// Split count for the 64 x 64 x 32 split-K tile: the modelled fastest among
+// those that keep every workgroup resident at once (at most four per CU) with
+// at least two k-tiles per split; one split is always a candidate.
+long long splits_64x64(long long tiles, int ktiles) {
+    long long best_s = 1;
+    double best_t = model_64x64_us(tiles, ktiles, 1, 1);
+    for (long long s = 2; s <= std::min<long long>(kMaxSplits, ktiles); ++s) {
+        const long long kt = (ktiles + s - 1) / s;
+        if ((ktiles + kt - 1) / kt != s) continue;   // same split as a smaller s
+        if (kt < 2 || tiles * s > 4LL * kNumCus) continue;
+        const double t = model_64x64_us(tiles, ktiles, 1, s);
+        if (t < best_t) {
+            best_s = s;
+            best_t = t;
+        }
+    }
+    return best_s;
+}
+
 // Shape class -> configuration, from per-configuration timings of the square
 // sweep, the layer shapes and the ragged shape on MI355X (bench.py
 // --sweep-configs):
@@ -1332,9 +1373,9 @@ double cu_balance(long long tiles, int slots = 1) {
 //                       one workgroup per CU;
 //   192..255 such tiles otherwise: 128 x 128 with 8 waves;
 //   else, by 64 x 64 tiles: >= 512 plain; 257..511 two k-groups, or split-K
-//                       over workgroups when those would fill under 70% of
-//                       the CU slots; <= 96 split-K over workgroups; else
-//                       four k-groups.
+//                       over workgroups when those would fill under 75% of
+//                       the CU slots; <= 256 four k-groups or split-K,
+//                       whichever the 64 x 64 timing model puts first.
 int select_config(char transA, char transB, int M, int N, int K) {
     if (M <= kSkinnyMaxM) return kCfgBand;
     auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
@@ -1375,10 +1416,12 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // 257..511 tiles of 64 x 64: two k-groups unless their workgroups would
     // leave the CU slots badly filled; then split-K over workgroups, whose
     // smaller workgroups spread more evenly.
-    if (t64 > kNumCus) return (double)t64 / (2 * kNumCus) >= 0.7 ? kCfg64Kg2 : kCfg64Split;
-    // Up to 96 tiles of 64 x 64 (n <= ~600): split-K over workgroups.
-    if (t64 <= 96) return kCfg64Split;
-    return kCfg64Kg4;
+    if (t64 > kNumCus) return (double)t64 / (2 * kNumCus) >= 0.75 ? kCfg64Kg2 : kCfg64Split;
+    // Up to 256 tiles of 64 x 64: four k-groups or split-K over workgroups,
+    // whichever the timing model puts first.
+    const int ktiles = (K + 31) / 32;
+    const double t_split = model_64x64_us(t64, ktiles, 1, splits_64x64(t64, ktiles));
+    return t_split < model_64x64_us(t64, ktiles, 4, 1) ? kCfg64Split : kCfg64Kg4;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1552,11 +1595,17 @@ hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int spl
     g.ws = nullptr;
     g.counters = nullptr;
     if (CFG::SPLIT && split_slots > 0) {
-        // Split-K over workgroups: about one workgroup per CU slot, at least
-        // four k-tiles per split, within the workspace.
+        // Split-K over workgroups: for 64 x 64 tiles the modelled best split;
+        // otherwise about one workgroup per CU slot with at least four
+        // k-tiles per split. Either within the workspace.
         const long long tiles = (long long)g.tiles_m * g.tiles_n;
-        long long S = ((long long)kNumCus * split_slots + tiles - 1) / tiles;
-        if (S > ktiles / 4) S = ktiles / 4;
+        long long S;
+        if constexpr (CFG::BM == 64 && CFG::BN == 64) {
+            S = splits_64x64(tiles, ktiles);
+        } else {
+            S = ((long long)kNumCus * split_slots + tiles - 1) / tiles;
+            if (S > ktiles / 4) S = ktiles / 4;
+        }
         if (S > kMaxSplits) S = kMaxSplits;
         if (S < 1) S = 1;
         while (S > 1 && tiles * S * CFG::BM * CFG::BN > (long long)kWsFloats) --S;

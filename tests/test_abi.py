@@ -128,7 +128,14 @@ def test_shape_class_selection():
     assert sel("N", "N", 1000, 1300, 700) == "mfma32_64x64x32_w2x2_splitk"
     assert sel("N", "N", 1280, 1280, 1280) == "mfma32_64x64x32_w2x2_kg2"
     assert sel("N", "N", 512, 512, 512) == "mfma32_64x64x32_w2x2_splitk"
-    assert sel("N", "N", 768, 768, 768) == "mfma32_64x64x32_w2x2_kg4"
+    # Up to 256 tiles of 64 x 64: split-K where the 64 x 64 timing model puts
+    # it ahead of four k-groups (short grids, long K).
+    assert sel("N", "N", 768, 768, 768) == "mfma32_64x64x32_w2x2_splitk"
+    assert sel("T", "T", 832, 832, 832) == "mfma32_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 2048, 256, 2048) == "mfma32_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 960, 960, 960) == "mfma32_64x64x32_w2x2_kg4"
+    # 361 tiles fill under 75% of two slots per CU: split-K.
+    assert sel("N", "N", 1216, 1216, 1216) == "mfma32_64x64x32_w2x2_splitk"
     # 144..255 tiles of 128 x 128 with enough k-work: stream-K, one workgroup per CU.
     assert sel("N", "N", 1792, 1792, 1792) == "mfma32_128x128x32_w4x2_streamk_1wg"
     assert sel("N", "N", 1536, 1536, 1536) == "mfma32_128x128x32_w4x2_streamk_1wg"
