@@ -292,6 +292,47 @@ def run_workload(name, steps, warmup):
     print(json.dumps(row), flush=True)
 
 
+PEAK_FP32_VECTOR_TFLOPS = 157.3    # FP32 vector FMA: 256 CU x 2.4 GHz x 256 FLOP/clk/CU
+
+
+def run_ladder(path, sizes=(1024, 4096)):
+    """The vector-ALU technique ladder (configs named valu_*), rung by rung,
+    beside the matrix-core path mi_sgemm picks, on square NN products with
+    alpha = 1, beta = 0: per-call time, TFLOP/s, fraction of the unpacked FP32
+    vector peak, and speed relative to the matrix-core path. One JSON object
+    per line."""
+    import fp32_gemm_nn_amd as mg
+    from synthetic import workloads as W
+
+    names = mg.config_names()
+    ladder = [i for i, n in enumerate(names) if n.startswith("valu_")]
+    with open(path, "w") as out:
+        for n in sizes:
+            case = W.Case(f"nn_{n}", "N", "N", n, n, n, 1.0, 0.0, seed=2)
+            prob = Problem(case)
+            rows = []
+            for cfg in [None, *ladder]:
+                _, first = time_problem(prob, 1, 1, config=cfg)
+                calls = max(3, min(2000, int(0.2 / max(first, 1e-6))))
+                _, ev = time_problem(prob, calls, 1, config=cfg)
+                per = ev / calls
+                chosen = mg.mi_sgemm_select_config("N", "N", n, n, n)
+                rows.append({"workload": case.name, "M": n, "N": n, "K": n,
+                             "kernel_config": names[chosen] if cfg is None else names[cfg],
+                             "unit": "matrix cores" if cfg is None else "vector ALUs",
+                             "calls": calls, "us_per_call": round(per * 1e6, 3),
+                             "TFLOPS": round(tflops(case.flops, per), 3)})
+            mfma_us = rows[0]["us_per_call"]
+            for row in rows:
+                row["pct_fp32_vector_peak"] = round(100 * row["TFLOPS"] / PEAK_FP32_VECTOR_TFLOPS, 2)
+                row["pct_fp32_matrix_peak"] = round(100 * row["TFLOPS"] / PEAK_FP32_MATRIX_TFLOPS, 2)
+                row["speed_vs_matrix_path"] = round(mfma_us / row["us_per_call"], 4)
+                out.write(json.dumps(row) + "\n")
+                out.flush()
+                print(json.dumps(row), file=sys.stderr, flush=True)
+            del prob
+
+
 def run_config_sweep(path, warmup=3):
     """Every kernel configuration on every workload (one JSON object per line):
     the data the shape-class rule in select_config is chosen from."""
@@ -328,6 +369,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep-configs", metavar="PATH",
                     help="also time every kernel configuration on every workload, to PATH")
+    ap.add_argument("--ladder", metavar="PATH",
+                    help="time the vector-ALU technique ladder (valu_* configs) beside the matrix-core path at "
+                         "1024^3 and 4096^3, to PATH, and exit")
     ap.add_argument("--workload", metavar="NAME",
                     help="time only this workload (a name from synthetic/workloads.py) with its chosen "
                          "kernel and print its numbers; for profiling one configuration at a time")
@@ -353,6 +397,9 @@ def main():
         return
     if args.workload:
         run_workload(args.workload, args.steps, args.warmup)
+        return
+    if args.ladder:
+        run_ladder(args.ladder)
         return
 
     case = W.HEADLINE

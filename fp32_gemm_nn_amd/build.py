@@ -1,7 +1,9 @@
 """Build the HIP library fp32_gemm_nn_amd/libmisgemm.so for gfx950.
 
 hipcc cross-compiles the device code without a GPU present. Packed-FP32 VALU
-instructions are switched off for all device code.
+instructions are switched off for all device code. The sources are compiled
+to objects in parallel (under fp32_gemm_nn_amd/_build/) and linked into one
+shared library.
 """
 from __future__ import annotations
 
@@ -11,13 +13,14 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "misgemm.hip")
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("misgemm.hip", "ladder.hip")]
+OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmisgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
@@ -25,10 +28,23 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    cmd = [HIPCC, *FLAGS, *(extra or []), SRC, "-o", LIB + ".tmp"]
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    procs = []
+    objs = []
+    for src in SRCS:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *(extra or []), "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd)))
+        objs.append(obj)
+    for cmd, p in procs:
+        if p.wait() != 0:
+            raise subprocess.CalledProcessError(p.returncode, cmd)
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -65,6 +65,7 @@
 #include <utility>
 
 #include "misgemm.h"
+#include "ladder.h"
 
 namespace {
 
@@ -1225,6 +1226,8 @@ enum ConfigId : int {
     kCfgStreamK2 = 17,
     kCfgStreamK256x128 = 18,
     kCfgStreamK128x256 = 19,
+    // The vector-ALU technique ladder (ladder.hip), forced only.
+    kCfgLadderFirst = 20,
 };
 
 struct ConfigInfo {
@@ -1253,10 +1256,15 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma32_128x128x32_w4x2_streamk_2wg", CfgL42S2::BM, CfgL42S2::BN, CfgL42S2::NT},
     {"mfma32_256x128x32_w4x2_streamk", CfgWS::BM, CfgWS::BN, CfgWS::NT},
     {"mfma32_128x256x32_w2x4_streamk", CfgTS::BM, CfgTS::BN, CfgTS::NT},
+    {"valu_naive", 4, 64, 256},
+    {"valu_lds32x32", 32, 32, 1024},
+    {"valu_block1d_64x64x8_tm8", 64, 64, 512},
+    {"valu_block2d_128x128x8_8x8", 128, 128, 256},
+    {"valu_vec2d_128x128x8_8x8_dbuf", 128, 128, 256},
 };
 constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-static_assert(kNumConfigs == kCfgStreamK128x256 + 1, "one ConfigId per kConfigs entry");
+static_assert(kNumConfigs == kCfgLadderFirst + misgemm_ladder::kNumRungs, "one ConfigId per kConfigs entry");
 static_assert(kConfigs[kCfg128].bm == CfgL::BM && kConfigs[kCfg128].bn == CfgL::BN && kConfigs[kCfg128].nt == CfgL::NT, "kConfigs order");
 static_assert(kConfigs[kCfg64].bm == CfgS::BM && kConfigs[kCfg64].bn == CfgS::BN && kConfigs[kCfg64].nt == CfgS::NT, "kConfigs order");
 static_assert(kConfigs[kCfg64Kg2].bm == CfgS2::BM && kConfigs[kCfg64Kg2].bn == CfgS2::BN && kConfigs[kCfg64Kg2].nt == CfgS2::NT, "kConfigs order");
@@ -1703,6 +1711,24 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     if ((config == kCfgSkinny16 || config == kCfgBand) && (M + 2 * 16 - 1) / (2 * 16) > 65535)
         return MISGEMM_TOO_LARGE;
     hipError_t err;
+    if (config >= kCfgLadderFirst) {
+        misgemm_ladder::LadderArgs la;
+        la.A = A;
+        la.B = B;
+        la.C = C;
+        la.M = M;
+        la.N = N;
+        la.K = K;
+        la.lda = lda;
+        la.ldb = ldb;
+        la.ldc = ldc;
+        la.alpha = alpha;
+        la.beta = beta;
+        la.vec_ab = g.vec_ab;
+        la.vec_c = g.vec_c;
+        err = misgemm_ladder::launch(config - kCfgLadderFirst, ta, tb, la, stream);
+        return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
+    }
     switch (config) {
         case kCfg128: err = launch_cfg<CfgL>(ta, tb, g, stream); break;
         case kCfg64: err = launch_cfg<CfgS>(ta, tb, g, stream); break;

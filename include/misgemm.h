@@ -7,9 +7,14 @@
  * "【CUDA】Sgemm单精度矩阵乘法" (klklkl10086.github.io), where
  * C_ij = sum_k A_ik B_kj and a product costs 2MNK floating-point operations.
  *
- * Every product is computed in FP32 on the CDNA4 matrix cores
+ * mi_sgemm computes every product in FP32 on the CDNA4 matrix cores
  * (v_mfma_f32_32x32x2_f32 / v_mfma_f32_16x16x4_f32): FP32 inputs, FP32
  * products and FP32 accumulation, with no reduced-precision emulation.
+ * The configurations named valu_* (reachable only through
+ * mi_sgemm_with_config) are the itan.pw page's technique ladder (its
+ * section 3: naive, LDS tiles, 1-D and 2-D register tiles, 16-byte loads
+ * with double-buffered LDS) on the vector ALUs, with FP32 fused
+ * multiply-adds in ascending k.
  *
  * Threading: every entry point is thread-safe. The only mutable state is the
  * set of split-K workspaces (one per device and stream, see mi_sgemm), which
@@ -93,8 +98,9 @@ int mi_sgemm(char transA, char transB, int M, int N, int K,
 /*
  * mi_sgemm_with_config: as mi_sgemm, but with the kernel configuration chosen
  * by the caller instead of by shape class (config ids 0 .. count-1 from
- * mi_sgemm_config_count). Meant for tests and tuning: any config computes the
- * same result for any valid shape. Returns MISGEMM_BAD_CONFIG for an unknown
+ * mi_sgemm_config_count). Meant for tests, tuning and baselines: any config
+ * computes the same result, to FP32 rounding, for any valid shape (the same
+ * bits on integer-valued inputs). Returns MISGEMM_BAD_CONFIG for an unknown
  * id, after the argument checks of mi_sgemm.
  */
 int mi_sgemm_with_config(int config, char transA, char transB, int M, int N, int K,

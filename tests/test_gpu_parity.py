@@ -340,6 +340,21 @@ def test_every_config_uniform_medium(config, ta, tb):
     compare(case, run_gpu(case, inp, config=config), run_oracle(case, inp), False)
 
 
+# --- the vector-ALU technique ladder at the workload shapes ---------------------------------
+
+LADDER = [i for i, n in enumerate(mg.config_names()) if n.startswith("valu_")]
+LADDER_CASES = [W.C1, W.C2_INT, *[c.with_(name="int_" + c.name, fill="int_rand", alpha=2.0, beta=-1.0)
+                                  for c in W.C5A]]
+
+
+@pytest.mark.parametrize("case", LADDER_CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("config", LADDER)
+def test_ladder_workloads(config, case):
+    note(f"ladder cfg{config} {case.name}")
+    inp = W.make_inputs(case)
+    compare(case, run_gpu(case, inp, config=config), run_oracle(case, inp), is_exact(case))
+
+
 # --- layouts: leading-dimension padding, alignment, poisoned padding ------------------------
 
 @pytest.mark.parametrize("ta,tb", OPS)
