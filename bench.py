@@ -268,8 +268,9 @@ def run_table(path, steps, warmup):
             del prob
 
 
-def run_workload(name, steps, warmup):
-    """One workload with its chosen kernel: one JSON line of its numbers."""
+def run_workload(name, steps, warmup, configs=None):
+    """One workload with its chosen kernel, or with each of `configs` (names
+    or ids) forced: one JSON line of numbers per kernel."""
     import fp32_gemm_nn_amd as mg
     from synthetic import workloads as W
 
@@ -279,17 +280,21 @@ def run_workload(name, steps, warmup):
     case = cases[name]
     skinny = case.M <= 32
     prob = Problem(case, copies=8 if skinny else 1)
-    _, ev = time_problem(prob, steps, warmup)
-    per = ev / steps
-    row = {"workload": case.name, "transA": case.transA, "transB": case.transB, "M": case.M, "N": case.N,
-           "K": case.K, "kernel_config": mg.mi_sgemm_config_name(
-               mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)),
-           "steps": steps, "us_per_call": round(per * 1e6, 3), "TFLOPS": round(tflops(case.flops, per), 3),
-           "pct_fp32_matrix_peak": round(100 * tflops(case.flops, per) / PEAK_FP32_MATRIX_TFLOPS, 2),
-           "GBps_algorithmic": round(case.algorithmic_bytes / per / 1e9, 1)}
-    if skinny:
-        row["pct_hbm_peak"] = round(100 * case.algorithmic_bytes / per / 1e9 / PEAK_HBM_GBPS, 2)
-    print(json.dumps(row), flush=True)
+    names = mg.config_names()
+    chosen = mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)
+    ids = [None] if not configs else [int(c) if str(c).isdigit() else names.index(c) for c in configs]
+    for cfg in ids:
+        _, ev = time_problem(prob, steps, warmup, config=cfg)
+        per = ev / steps
+        row = {"workload": case.name, "transA": case.transA, "transB": case.transB, "M": case.M, "N": case.N,
+               "K": case.K, "kernel_config": names[chosen if cfg is None else cfg],
+               "chosen": cfg is None or cfg == chosen,
+               "steps": steps, "us_per_call": round(per * 1e6, 3), "TFLOPS": round(tflops(case.flops, per), 3),
+               "pct_fp32_matrix_peak": round(100 * tflops(case.flops, per) / PEAK_FP32_MATRIX_TFLOPS, 2),
+               "GBps_algorithmic": round(case.algorithmic_bytes / per / 1e9, 1)}
+        if skinny:
+            row["pct_hbm_peak"] = round(100 * case.algorithmic_bytes / per / 1e9 / PEAK_HBM_GBPS, 2)
+        print(json.dumps(row), flush=True)
 
 
 PEAK_FP32_VECTOR_TFLOPS = 157.3    # FP32 vector FMA: 256 CU x 2.4 GHz x 256 FLOP/clk/CU
@@ -369,6 +374,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--sweep-configs", metavar="PATH",
                     help="also time every kernel configuration on every workload, to PATH")
+    ap.add_argument("--config", action="append", metavar="NAME_OR_ID",
+                    help="with --workload: time this kernel configuration instead of the chosen one "
+                         "(repeatable)")
     ap.add_argument("--ladder", metavar="PATH",
                     help="time the vector-ALU technique ladder (valu_* configs) beside the matrix-core path at "
                          "1024^3 and 4096^3, to PATH, and exit")
@@ -396,7 +404,7 @@ def main():
         run_copy(args.steps, args.warmup)
         return
     if args.workload:
-        run_workload(args.workload, args.steps, args.warmup)
+        run_workload(args.workload, args.steps, args.warmup, args.config)
         return
     if args.ladder:
         run_ladder(args.ladder)

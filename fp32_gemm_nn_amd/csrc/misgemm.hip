@@ -105,8 +105,11 @@ struct GemmArgs {
 // groups of waves take alternate k-tiles (split-K inside the workgroup), each
 // with its own LDS buffers, and are summed at the end in group order.
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1, int EU_ = 0, bool SPLIT_ = false,
-          bool STREAMK_ = false>
+          bool STREAMK_ = false, bool DL_ = false>
 struct TileCfg {
+    // DL: the straight-line rounds move tiles global -> LDS directly
+    // (global_load_lds_dwordx4), with unpadded, chunk-swizzled LDS rows.
+    static constexpr bool DL = DL_;
     // SPLIT: the kernel carries the split-K-over-workgroups reduction.
     static constexpr bool SPLIT = SPLIT_;
     // STREAMK: one workgroup per CU walks an equal share of all (tile,
@@ -147,14 +150,26 @@ template <> struct LdsVec<4> {
 // One R x CC tile of a stored row-major matrix, moved global -> registers ->
 // LDS in 16-byte chunks. Thread t handles chunks t, t+NT, ...; a chunk is four
 // consecutive columns of one row. LDS layout: [R][CC + kLdsPad].
-template <int R, int CC, int NT>
+//
+// DL layout (for direct global -> LDS loads, which write a wave's 64 chunks
+// to 1 KB of consecutive LDS): rows are unpadded, [R][CC]. When SWZ (a
+// k-contiguous tile, read as 16-byte runs down 8 consecutive rows), chunk c
+// of row r sits at chunk position c ^ swz(r), so those 8 reads fall on 8
+// different 16-byte bank groups, as the padding achieves otherwise.
+template <int R, int CC, int NT, bool DL = false, bool SWZ = false>
 struct TileCopy {
     static constexpr int CPR = CC / 4;                  // chunks per row
     static constexpr int CHUNKS = R * CPR;
     static constexpr int PER_THREAD = CHUNKS / NT;
-    static constexpr int STRIDE = CC + kLdsPad;
+    static constexpr int STRIDE = DL ? CC : CC + kLdsPad;
     static constexpr int LDS_FLOATS = R * STRIDE;
     static_assert(CC % 4 == 0 && CHUNKS % NT == 0, "tile must split evenly over the threads");
+    static_assert(!SWZ || (DL && (CPR == 4 || CPR == 8)), "swizzle is for 16- or 32-wide k-contiguous rows");
+    static_assert(!DL || NT % 64 == 0, "direct loads are issued per wave");
+
+    // Chunk position of chunk c in row r (SWZ), and its LDS float offset.
+    static __device__ __forceinline__ int swz(int r) { return SWZ ? (r / (8 / CPR)) & (CPR - 1) : 0; }
+    static __device__ __forceinline__ int at(int r, int c) { return r * STRIDE + ((c / 4) ^ swz(r)) * 4; }
 
     f32x4 v[PER_THREAD];
 
@@ -193,7 +208,23 @@ struct TileCopy {
         for (int j = 0; j < PER_THREAD; ++j) {
             const int idx = tid + NT * j;
             const int r = idx / CPR, c = (idx % CPR) * 4;
-            *reinterpret_cast<f32x4 *>(lds + r * STRIDE + c) = v[j];
+            *reinterpret_cast<f32x4 *>(lds + at(r, c)) = v[j];
+        }
+    }
+
+    // DL layout, unguarded tile: each wave's j-th instruction fills LDS chunk
+    // positions NT*j + 64*wave .. +63 (lane l the l-th), from the chunks that
+    // belong there. The caller follows the batch with a compiler memory
+    // barrier (the LDS writes are invisible to the compiler) and waits for
+    // vmcnt before the workgroup barrier that publishes the tile.
+    __device__ __forceinline__ void load_direct(const float *__restrict__ base, int ld, float *lds, int tid) const {
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int idx = tid + NT * j;
+            const int r = idx / CPR, p = idx % CPR;
+            const int c = p ^ swz(r);
+            __builtin_amdgcn_global_load_lds(base + (size_t)r * ld + 4 * c, lds + 4 * (NT * j + (tid & ~63)), 16, 0,
+                                             0);
         }
     }
 };
@@ -276,6 +307,18 @@ struct Frag {
     float a[FM][4];
     float b[FN][4];
 
+    // Float offset inside a k-contiguous LDS row of the lane's q-group: k =
+    // lh*HB + 4q, at its swizzled chunk position in the DL layout (the row is
+    // li plus a multiple of 8, so its swizzle depends on li alone).
+    static __device__ __forceinline__ int kofs(int li, int lh, int q) {
+        if constexpr (CFG::DL) {
+            constexpr int CPR = CFG::BK / 4;
+            return (((lh * HB + 4 * q) / 4) ^ ((li / (8 / CPR)) & (CPR - 1))) * 4;
+        } else {
+            return lh * HB + 4 * q;
+        }
+    }
+
     // as/bs: LDS tiles of one k-tile, row strides AS/BS.
     template <int AS, int BS>
     __device__ __forceinline__ void read(const float *as, const float *bs, int q, int wm, int wn, int li, int lh) {
@@ -283,7 +326,7 @@ struct Frag {
             // k-contiguous A tile [m][k]: block blk, lane row li is m = 32*blk + li.
 #pragma unroll
             for (int blk = 0; blk < FM; ++blk)
-                LdsVec<4>::get(as + (wm * WTM + 32 * blk + li) * AS + lh * HB + 4 * q, a[blk]);
+                LdsVec<4>::get(as + (wm * WTM + 32 * blk + li) * AS + kofs(li, lh, q), a[blk]);
         } else {
             // m-contiguous A tile [k][m]: block blk, lane row li is m = FM*li + blk.
 #pragma unroll
@@ -298,7 +341,7 @@ struct Frag {
             // k-contiguous B tile [n][k]: block blk, lane column li is n = 32*blk + li.
 #pragma unroll
             for (int blk = 0; blk < FN; ++blk)
-                LdsVec<4>::get(bs + (wn * WTN + 32 * blk + li) * BS + lh * HB + 4 * q, b[blk]);
+                LdsVec<4>::get(bs + (wn * WTN + 32 * blk + li) * BS + kofs(li, lh, q), b[blk]);
         } else {
             // n-contiguous B tile [k][n]: block blk, lane column li is n = FN*li + blk.
 #pragma unroll
@@ -381,8 +424,8 @@ void sgemm_mfma32(GemmArgs g) {
     static_assert(Q % 2 == 0, "fragment buffers alternate, so the q-group count must be even");
     // Stored tile shapes: A is BM x BK ('N', k contiguous) or BK x BM ('T',
     // m contiguous); B is BK x BN ('N', n contiguous) or BN x BK ('T').
-    using ACopy = TileCopy<TA ? BK : BM, TA ? BM : BK, NTG>;
-    using BCopy = TileCopy<TB ? BN : BK, TB ? BK : BN, NTG>;
+    using ACopy = TileCopy<TA ? BK : BM, TA ? BM : BK, NTG, CFG::DL, CFG::DL && !TA>;
+    using BCopy = TileCopy<TB ? BN : BK, TB ? BK : BN, NTG, CFG::DL, CFG::DL && TB>;
     using F = Frag<CFG, TA, TB>;
     constexpr int A_FLOATS = ACopy::LDS_FLOATS, B_FLOATS = BCopy::LDS_FLOATS;
     constexpr int AS = ACopy::STRIDE, BS = BCopy::STRIDE;
@@ -480,23 +523,35 @@ void sgemm_mfma32(GemmArgs g) {
                 const float *bs = b_lds + cur * B_FLOATS;
                 float *as_n = a_lds + nxt * A_FLOATS;
                 float *bs_n = b_lds + nxt * B_FLOATS;
-                fetch_fast(kt_begin + (r + 1) * KG + grp);
+                const int kt_next = kt_begin + (r + 1) * KG + grp;
+                if constexpr (CFG::DL) {
+                    // The other buffer was last read before the previous
+                    // round's barrier, so the next tile can land in it now.
+                    ca.load_direct(a_ptr + kt_next * a_step, g.lda, as_n, gtid);
+                    cb.load_direct(b_ptr + kt_next * b_step, g.ldb, bs_n, gtid);
+                    asm volatile("" ::: "memory");
+                } else {
+                    fetch_fast(kt_next);
+                }
 #pragma unroll
                 for (int q = 0; q < Q; q += 2) {
                     f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
                     f0.mma(acc);
                     if (q + 2 < Q) {
                         f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
-                    } else {
+                    } else if constexpr (!CFG::DL) {
                         ca.store(as_n, gtid);
                         cb.store(bs_n, gtid);
                     }
                     f1.mma(acc);
                 }
                 // DS reads per q-group: FM (or FN) 16-byte reads of a k-contiguous
-                // tile, four narrow reads of an m/n-contiguous one.
-                schedule_iteration<4 * FM * FN, Q, ACopy::PER_THREAD + BCopy::PER_THREAD,
-                                   (TA ? 4 : FM) + (TB ? FN : 4), ACopy::PER_THREAD + BCopy::PER_THREAD>();
+                // tile, four narrow reads of an m/n-contiguous one. Direct loads
+                // are issued before the round's first reads and leave no writes.
+                constexpr int COPIES = CFG::DL ? 0 : ACopy::PER_THREAD + BCopy::PER_THREAD;
+                schedule_iteration<4 * FM * FN, Q, COPIES, (TA ? 4 : FM) + (TB ? FN : 4), COPIES>();
+                // Direct loads complete (vmcnt) before the barrier publishes them.
+                if constexpr (CFG::DL) __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
                 f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
             }
@@ -1203,6 +1258,9 @@ using CfgL42S1 = TileCfg<128, 128, 32, 4, 2, 1, 2, false, true>;
 using CfgL42S2 = TileCfg<128, 128, 32, 4, 2, 1, 4, false, true>;
 using CfgWS = TileCfg<256, 128, 32, 4, 2, 1, 0, false, true>;   // one workgroup per CU
 using CfgTS = TileCfg<128, 256, 32, 2, 4, 1, 0, false, true>;
+// Direct global -> LDS loads in the straight-line rounds.
+using CfgQ32D = TileCfg<256, 256, 32, 4, 2, 1, 0, false, false, true>;
+using CfgL42D = TileCfg<128, 128, 32, 4, 2, 1, 4, false, false, true>;
 
 // Config ids: the index of each entry of kConfigs below.
 enum ConfigId : int {
@@ -1228,6 +1286,9 @@ enum ConfigId : int {
     kCfgStreamK128x256 = 19,
     // The vector-ALU technique ladder (ladder.hip), forced only.
     kCfgLadderFirst = 20,
+    kCfgLadderLast = kCfgLadderFirst + misgemm_ladder::kNumRungs - 1,
+    kCfg256x256Dl = 25,
+    kCfg128W42Dl = 26,
 };
 
 struct ConfigInfo {
@@ -1261,10 +1322,13 @@ constexpr ConfigInfo kConfigs[] = {
     {"valu_block1d_64x64x8_tm8", 64, 64, 512},
     {"valu_block2d_128x128x8_8x8", 128, 128, 256},
     {"valu_vec2d_128x128x8_8x8_dbuf", 128, 128, 256},
+    {"mfma32_256x256x32_w4x2_dl", CfgQ32D::BM, CfgQ32D::BN, CfgQ32D::NT},
+    {"mfma32_128x128x32_w4x2_dl", CfgL42D::BM, CfgL42D::BN, CfgL42D::NT},
 };
 constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-static_assert(kNumConfigs == kCfgLadderFirst + misgemm_ladder::kNumRungs, "one ConfigId per kConfigs entry");
+static_assert(kNumConfigs == kCfg128W42Dl + 1, "one ConfigId per kConfigs entry");
+static_assert(kCfgLadderLast + 1 == kCfg256x256Dl, "the ladder ids are contiguous");
 static_assert(kConfigs[kCfg128].bm == CfgL::BM && kConfigs[kCfg128].bn == CfgL::BN && kConfigs[kCfg128].nt == CfgL::NT, "kConfigs order");
 static_assert(kConfigs[kCfg64].bm == CfgS::BM && kConfigs[kCfg64].bn == CfgS::BN && kConfigs[kCfg64].nt == CfgS::NT, "kConfigs order");
 static_assert(kConfigs[kCfg64Kg2].bm == CfgS2::BM && kConfigs[kCfg64Kg2].bn == CfgS2::BN && kConfigs[kCfg64Kg2].nt == CfgS2::NT, "kConfigs order");
@@ -1283,6 +1347,8 @@ static_assert(kConfigs[kCfgStreamK1].bm == CfgL42S1::BM && kConfigs[kCfgStreamK1
 static_assert(kConfigs[kCfgStreamK2].bm == CfgL42S2::BM && kConfigs[kCfgStreamK2].bn == CfgL42S2::BN && kConfigs[kCfgStreamK2].nt == CfgL42S2::NT, "kConfigs order");
 static_assert(kConfigs[kCfgStreamK256x128].bm == CfgWS::BM && kConfigs[kCfgStreamK256x128].bn == CfgWS::BN && kConfigs[kCfgStreamK256x128].nt == CfgWS::NT, "kConfigs order");
 static_assert(kConfigs[kCfgStreamK128x256].bm == CfgTS::BM && kConfigs[kCfgStreamK128x256].bn == CfgTS::BN && kConfigs[kCfgStreamK128x256].nt == CfgTS::NT, "kConfigs order");
+static_assert(kConfigs[kCfg256x256Dl].bm == CfgQ32D::BM && kConfigs[kCfg256x256Dl].bn == CfgQ32D::BN && kConfigs[kCfg256x256Dl].nt == CfgQ32D::NT, "kConfigs order");
+static_assert(kConfigs[kCfg128W42Dl].bm == CfgL42D::BM && kConfigs[kCfg128W42Dl].bn == CfgL42D::BN && kConfigs[kCfg128W42Dl].nt == CfgL42D::NT, "kConfigs order");
 constexpr int kNumCus = 256;
 
 bool op_n(char t) { return t == 'N' || t == 'n'; }
@@ -1390,6 +1456,9 @@ int select_config(char transA, char transB, int M, int N, int K) {
     const long long t128 = tiles(128, 128), t64 = tiles(64, 64);
     // Stream-K work: 128 x 128 x 32 iterations.
     const long long sk_iters = t128 * ((K + 31) / 32);
+    // The 128 x 128 tile with only A transposed loads directly into LDS:
+    // 5-20% faster there (2048^3 TN: 129 vs 154 us), 1-3% slower elsewhere.
+    const int cfg128 = op_t(transA) && op_n(transB) ? kCfg128W42Dl : kCfg128W42;
     if (t128 >= kNumCus) {
         const bool ta = op_t(transA), tb = op_t(transB);
         // Big tiles (one workgroup per CU) lose to 128 x 128 (two per CU)
@@ -1399,7 +1468,9 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const bool big_ok = !(K < 2048 && t128 < 4 * kNumCus) || (ta && !tb);
         const bool tt = ta && tb;
         const bool wide = !tt && M < N;    // 128 x 256 rather than 256 x 128
-        const double s_q = big_ok ? (tt ? 1.0 : 1.044) * cu_balance(tiles(256, 256)) : -1.0;
+        // With both transposed, the 256 x 256 tile with direct-to-LDS loads
+        // (the register-staged one spills): 960 vs 989 us for 256 x 128 at 4096^3.
+        const double s_q = big_ok ? (tt ? 1.065 : 1.044) * cu_balance(tiles(256, 256)) : -1.0;
         const double s_b4 = big_ok ? (tt ? 1.0 : 1.038) * cu_balance(tiles(128, 256), 2) : -1.0;
         const double s_b8 = big_ok ? (tt ? 1.034 : 1.024) * cu_balance(wide ? tiles(128, 256) : tiles(256, 128)) : -1.0;
         const double s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
@@ -1409,17 +1480,17 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const double s_skb = (sk_ok && big_ok) ? 0.955 : -1.0;
         const double s_sk = sk_ok ? 0.925 : -1.0;
         const double best = fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(s_128, s_64));
-        if (best == s_q) return kCfg256x256;
+        if (best == s_q) return tt ? kCfg256x256Dl : kCfg256x256;
         if (best == s_skb) return wide ? kCfgStreamK128x256 : kCfgStreamK256x128;
         if (best == s_sk) return kCfgStreamK2;
         if (best == s_b4) return kCfg128x256x16;
         if (best == s_b8) return wide ? kCfg128x256 : kCfg256x128;
-        return best == s_128 ? kCfg128W42 : kCfg64;
+        return best == s_128 ? cfg128 : kCfg64;
     }
     // 144..255 tiles of 128 x 128 with at least 20 k-tiles per workgroup:
     // stream-K, one workgroup per CU.
     if (t128 >= 144 && sk_iters >= 20LL * kNumCus) return kCfgStreamK1;
-    if (t128 >= 3 * kNumCus / 4) return kCfg128W42;
+    if (t128 >= 3 * kNumCus / 4) return cfg128;
     if (t64 >= 2 * kNumCus) return kCfg64;
     // 257..511 tiles of 64 x 64: two k-groups unless their workgroups would
     // leave the CU slots badly filled; then split-K over workgroups, whose
@@ -1711,7 +1782,7 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     if ((config == kCfgSkinny16 || config == kCfgBand) && (M + 2 * 16 - 1) / (2 * 16) > 65535)
         return MISGEMM_TOO_LARGE;
     hipError_t err;
-    if (config >= kCfgLadderFirst) {
+    if (config >= kCfgLadderFirst && config <= kCfgLadderLast) {
         misgemm_ladder::LadderArgs la;
         la.A = A;
         la.B = B;
@@ -1749,6 +1820,8 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case kCfgStreamK1: err = launch_cfg<CfgL42S1>(ta, tb, g, stream); break;
         case kCfgStreamK2: err = launch_cfg<CfgL42S2>(ta, tb, g, stream); break;
         case kCfgStreamK256x128: err = launch_cfg<CfgWS>(ta, tb, g, stream); break;
+        case kCfg256x256Dl: err = launch_cfg<CfgQ32D>(ta, tb, g, stream); break;
+        case kCfg128W42Dl: err = launch_cfg<CfgL42D>(ta, tb, g, stream); break;
         default: err = launch_cfg<CfgTS>(ta, tb, g, stream); break;   // kCfgStreamK128x256
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;

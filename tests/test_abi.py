@@ -112,10 +112,15 @@ def test_shape_class_selection():
     # 4096^2 output: 256 tiles of 256 x 256, one per CU.
     assert sel("N", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
     assert sel("T", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
-    # Both transposed: 256 x 128 is the big tile that pays.
     assert sel("N", "T", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
-    assert sel("T", "T", 4096, 4096, 4096) == "mfma32_256x128x32_w4x2"
+    # Both transposed: the 256 x 256 tile with direct-to-LDS loads.
+    assert sel("T", "T", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2_dl"
+    assert sel("T", "T", 4096, 4096, 1024) == "mfma32_256x256x32_w4x2_dl"
     assert sel("T", "T", 2048, 4096, 2048) == "mfma32_256x128x32_w4x2"
+    # Only A transposed: the 128 x 128 tile loads directly into LDS.
+    assert sel("T", "N", 2048, 2048, 2048) == "mfma32_128x128x32_w4x2_dl"
+    assert sel("T", "N", 2048, 2048, 4096) == "mfma32_128x128x32_w4x2_dl"
+    assert sel("N", "N", 2048, 2048, 2048) == "mfma32_128x128x32_w4x2"
     # 2048 x 4096 x 1024: short K on a grid that fills the chip once: 128 x 128
     # (two workgroups per CU), except with only A transposed.
     assert sel("N", "N", 2048, 4096, 1024) == "mfma32_128x128x32_w4x2"
