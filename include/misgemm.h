@@ -80,6 +80,13 @@ extern "C" {
  * one. If it cannot be allocated the kernel runs unsplit. No other call
  * allocates or frees memory.
  *
+ * Graph capture: a call may be captured into a HIP graph and replayed. It
+ * enqueues kernels only (no memset); split-K and stream-K kernels reset
+ * their own counters. Make one eager call that splits on the capture stream
+ * first, so that its workspace exists before capture (otherwise the captured
+ * call runs unsplit). Replays use that stream's workspace: do not run them
+ * concurrently with other calls on that stream.
+ *
  * Alignment: any pointer and leading dimension is accepted. 16-byte aligned
  * pointers with lda, ldb, ldc multiples of 4 take the dwordx4 path.
  *
