@@ -1558,6 +1558,12 @@ const Workspace *get_workspace(hipStream_t stream) {
     auto key = std::make_pair(dev, stream);
     auto it = g_ws.find(key);
     if (it != g_ws.end()) return &it->second;
+    // No allocation while the stream is being captured into a graph: the
+    // captured call runs unsplit instead.
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (stream != nullptr &&
+        (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone))
+        return nullptr;
     DeviceGuard on_dev(dev);
     if (!on_dev.ok) return nullptr;
     Workspace w;

@@ -70,3 +70,28 @@ def test_graph_replays_match_eager(case):
         torch.cuda.synchronize()
         assert torch.equal(C, want[k]), f"replay {rep} differs from the eager result"
     del graph
+
+
+def test_capture_without_workspace_runs_unsplit():
+    """Captured on a stream with no workspace yet, a split-K call runs unsplit
+    (no allocation during capture); on integer inputs every summation order
+    gives the same bits, so replays must equal the eager split result."""
+    case = W.C1.with_(name="int_c1_graph", fill="int_rand")
+    inp = W.make_inputs(case)
+    A, B = torch.from_numpy(inp.A).cuda(), torch.from_numpy(inp.B).cuda()
+    want = torch.from_numpy(inp.C.copy()).cuda()
+    mg.sgemm(case.transA, case.transB, case.alpha, A, B, case.beta, want)     # eager, split
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    C = torch.full_like(want, float("nan"))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        mg.sgemm(case.transA, case.transB, case.alpha, A, B, case.beta, C, stream=stream.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, want), f"replay {rep}"
+    del graph
