@@ -959,13 +959,14 @@ constexpr int kBandWaves = 8;
 constexpr int kMaxSplits = 32;
 // Waves per workgroup. One row block: sixteen on the unguarded path (more
 // loads in flight per CU; its fragments fit 128 registers), eight on the
-// guarded one. Two row blocks: four, so each wave may use 512 registers (the
-// fragments need ~260) and the LDS partial blocks fit.
+// guarded one. Two row blocks: eight on the unguarded path (one chunk per
+// buffer; the 8 x 16 KB LDS partial blocks fit), four on the guarded one, so
+// each wave may use 512 registers (its fragments need ~260).
 template <int MB, bool FAST> constexpr int band_waves() {
-    return MB == 1 ? (FAST ? 2 * kBandWaves : kBandWaves) : kBandWaves / 2;
+    return MB == 1 ? (FAST ? 2 * kBandWaves : kBandWaves) : (FAST ? kBandWaves : kBandWaves / 2);
 }
-// 16-row chunks per register buffer: one with sixteen waves, else two.
-template <int MB, bool FAST> constexpr int band_chunks() { return MB == 1 && FAST ? 1 : 2; }
+// 16-row chunks per register buffer: one on the unguarded path, else two.
+template <int MB, bool FAST> constexpr int band_chunks() { return FAST ? 1 : 2; }
 
 struct SplitArgs {
     GemmArgs g;
@@ -982,9 +983,9 @@ struct BandFrag {
     float a[kBandChunks][MB][4];
 
     // Chunk u covers k0 = kc + 16u .. +15, valid below kend. FAST: the host
-    // has checked that every band lies inside N, every chunk below kend, all
-    // 16*MB rows of A exist and the pointers allow 16-byte loads, so nothing
-    // is checked per element.
+    // has checked that every band lies inside N, every chunk below kend and
+    // the pointers allow 16-byte loads, so no load of B is checked; rows of A
+    // at or beyond M (A is small and stays in cache) read as zero.
     __device__ __forceinline__ void load(const GemmArgs &g, int m0, int n0, int c, int q, int kc, int kend,
                                          bool vec) {
         const int M = g.M, N = g.N, lda = g.lda, ldb = g.ldb;
@@ -1041,12 +1042,13 @@ struct BandFrag {
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = m0 + 16 * mb + c;
                 if (FAST && !TA) {
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
+                    f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    if (row < M) v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) a[u][mb][j] = v[j];
                 } else if (FAST) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) a[u][mb][j] = g.A[(size_t)(kq + j) * lda + row];
+                    for (int j = 0; j < 4; ++j) a[u][mb][j] = row < M ? g.A[(size_t)(kq + j) * lda + row] : 0.0f;
                 } else if (!TA && vec && row < M && kq + 3 < kend) {
                     const f32x4 v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
 #pragma unroll
@@ -1427,7 +1429,7 @@ long long splits_64x64(long long tiles, int ktiles) {
 // Shape class -> configuration, from per-configuration timings of the square
 // sweep, the layer shapes and the ragged shape on MI355X (bench.py
 // --sweep-configs):
-//   M <= 32             skinny band kernel (HBM-bound);
+//   M <= 32, N >= 128   skinny band kernel (HBM-bound);
 //   >= 256 tiles of 128 x 128: the best-scoring of
 //                       256 x 256 with 8 waves (one per CU; B not
 //                         transposed)                        1.044 x balance
@@ -1451,7 +1453,9 @@ long long splits_64x64(long long tiles, int ktiles) {
 //                       the CU slots; <= 256 four k-groups or split-K,
 //                       whichever the 64 x 64 timing model puts first.
 int select_config(char transA, char transB, int M, int N, int K) {
-    if (M <= kSkinnyMaxM) return kCfgBand;
+    // Few rows: the band kernel streams op(B) once; below one 128-column band
+    // its padding costs more than a tile kernel (32 x 64 x 64: 8.9 vs 5.6 us).
+    if (M <= kSkinnyMaxM && N >= kBandCols) return kCfgBand;
     auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     const long long t128 = tiles(128, 128), t64 = tiles(64, 64);
     // Stream-K work: 128 x 128 x 32 iterations.
@@ -1592,7 +1596,8 @@ int band_splits(int M, int N, int K, int mb, bool fast) {
     const long long bands = (N + kBandCols - 1) / kBandCols;
     const long long yb = (M + 16 * mb - 1) / (16 * mb);
     const long long tiles = bands * yb;
-    const int waves = mb == 1 ? (fast ? band_waves<1, true>() : band_waves<1, false>()) : band_waves<2, false>();
+    const int waves = mb == 1 ? (fast ? band_waves<1, true>() : band_waves<1, false>())
+                              : (fast ? band_waves<2, true>() : band_waves<2, false>());
     const long long lds_bytes = (long long)waves * 16 * mb * kBandCols * 4;
     const long long per_cu = lds_bytes > 80 * 1024 ? 1 : 2;
     long long S = (per_cu * kNumCus + tiles - 1) / tiles;
@@ -1627,9 +1632,8 @@ hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) 
     sa.g = g;
     sa.ws = nullptr;
     sa.counters = nullptr;
-    // Unguarded instantiation: whole bands, whole 16-row chunks, whole row
-    // blocks, 16-byte loads (one row block only).
-    const bool fast = mb == 1 && g.vec_ab && g.N % kBandCols == 0 && g.K % 16 == 0 && g.M % 16 == 0;
+    // Unguarded instantiation: whole bands, whole 16-row chunks, 16-byte loads.
+    const bool fast = g.vec_ab && g.N % kBandCols == 0 && g.K % 16 == 0;
     int S = band_splits(g.M, g.N, g.K, mb, fast);
     if (S > 1) {
         const Workspace *w = get_workspace(stream);
@@ -1646,7 +1650,7 @@ hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) 
     sa.splits = S;
     sa.rows_per_split = rps;
     if (mb == 1) return fast ? launch_band_mb<1, true>(ta, tb, sa, stream) : launch_band_mb<1, false>(ta, tb, sa, stream);
-    return launch_band_mb<2, false>(ta, tb, sa, stream);
+    return fast ? launch_band_mb<2, true>(ta, tb, sa, stream) : launch_band_mb<2, false>(ta, tb, sa, stream);
 }
 
 template <int MB, bool TA, bool TB>

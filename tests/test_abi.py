@@ -162,7 +162,10 @@ def test_shape_class_selection():
     assert sel("N", "N", 2304, 3328, 2048) == "mfma32_128x256x32_w2x4_streamk"
     # M <= 32: the skinny, bandwidth-bound kernel.
     assert "skinny" in sel("N", "N", 16, 4096, 4096)
-    assert "skinny" in sel("T", "T", 32, 100, 7)
+    assert "skinny" in sel("T", "T", 32, 128, 7)
+    # ... but not below one 128-column band.
+    assert "skinny" not in sel("T", "T", 32, 100, 7)
+    assert "skinny" not in sel("N", "N", 32, 64, 64)
     assert "skinny" not in sel("N", "N", 33, 4096, 4096)
     assert mg.mi_sgemm_select_config("Z", "N", 1, 1, 1) == -1
     assert mg.mi_sgemm_select_config("N", "N", 1, 1, -1) == -5
