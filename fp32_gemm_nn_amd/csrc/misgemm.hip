@@ -1041,14 +1041,19 @@ struct BandFrag {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = m0 + 16 * mb + c;
+                // Unguarded path: load from a row clamped into range (no branch
+                // in the streaming loop), then select zero past M.
+                const int row_c = row < M ? row : M - 1;
                 if (FAST && !TA) {
-                    f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    if (row < M) v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row_c * lda + kq);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) a[u][mb][j] = v[j];
+                    for (int j = 0; j < 4; ++j) a[u][mb][j] = row < M ? v[j] : 0.0f;
                 } else if (FAST) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) a[u][mb][j] = row < M ? g.A[(size_t)(kq + j) * lda + row] : 0.0f;
+                    for (int j = 0; j < 4; ++j) {
+                        const float v = g.A[(size_t)(kq + j) * lda + row_c];
+                        a[u][mb][j] = row < M ? v : 0.0f;
+                    }
                 } else if (!TA && vec && row < M && kq + 3 < kend) {
                     const f32x4 v = *reinterpret_cast<const f32x4 *>(g.A + (size_t)row * lda + kq);
 #pragma unroll

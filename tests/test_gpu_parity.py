@@ -166,7 +166,10 @@ BAND = mg.config_names().index("skinny_mfma16_band128_splitk")
 
 @pytest.mark.parametrize("ta,tb", OPS)
 @pytest.mark.parametrize("M,N,K", [(16, 4096, 4096), (7, 1000, 3001), (32, 130, 17), (17, 4096, 2048),
-                                   (1, 65, 100000), (24, 640, 640)])
+                                   (1, 65, 100000), (24, 640, 640),
+                                   # unguarded B streaming with rows of A beyond M (one and two row blocks)
+                                   (1, 1024, 4096), (5, 512, 2048), (12, 512, 1024), (28, 384, 512),
+                                   (31, 256, 4096)])
 def test_band_split_k(ta, tb, M, N, K):
     """Split-K band kernel: integer inputs bit-exact, whatever the split."""
     case = W.Case(f"band_{ta}{tb}_{M}x{N}x{K}", ta, tb, M, N, K, 1.0, -1.0, seed=50 + M, fill="int_rand")
