@@ -126,6 +126,32 @@ def _ld(t) -> int:
     return max(int(t.stride(0)), int(t.shape[1]), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
 
 
+def _overlaps(x, y) -> bool:
+    """Whether two 2-D tensors with contiguous rows share any element's memory
+    (C must not overlap A or B). Row i of x covers bytes [x0 + i*sx, x0 + i*sx + wx);
+    for each row of x the rows of y that could intersect it form one index
+    range, so the test is exact (padding between rows is not counted) and
+    linear in the rows of x."""
+    import numpy as np
+
+    if x.numel() == 0 or y.numel() == 0:
+        return False
+    es = x.element_size()
+
+    def rows(t):
+        return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else 1) * es, t.shape[1] * es, t.shape[0]
+
+    x0, sx, wx, rx = rows(x)
+    y0, sy, wy, ry = rows(y)
+    if x0 + (rx - 1) * sx + wx <= y0 or y0 + (ry - 1) * sy + wy <= x0:
+        return False
+    start = x0 + sx * np.arange(rx, dtype=np.int64)
+    # Rows j of y with y0 + j*sy < start + wx and y0 + j*sy + wy > start.
+    j_hi = np.minimum((start + wx - y0 - 1) // sy, ry - 1)
+    j_lo = np.maximum((start - y0 - wy) // sy + 1, 0)
+    return bool(np.any(j_lo <= j_hi))
+
+
 def sgemm(transA: str, transB: str, alpha: float, A, B, beta: float, C, stream=None, config=None):
     """C <- alpha*op(A)@op(B) + beta*C on float32 device tensors (row-major views).
 
@@ -141,6 +167,10 @@ def sgemm(transA: str, transB: str, alpha: float, A, B, beta: float, C, stream=N
             raise TypeError(f"{name} must be float32")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be a device tensor")
+    if not (A.device == B.device == C.device):
+        raise ValueError(f"A, B and C must be on one device (got {A.device}, {B.device}, {C.device})")
+    if _overlaps(C, A) or _overlaps(C, B):
+        raise ValueError("C must not overlap A or B")
     ta = transA in ("T", "t", "C", "c")
     tb = transB in ("T", "t", "C", "c")
     M, N = int(C.shape[0]), int(C.shape[1])

@@ -192,3 +192,37 @@ def test_one_hip_runtime_when_library_is_loaded_first():
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.split() == ["1", "1"], out.stdout
+
+
+def test_wrapper_overlap_check():
+    """The tensor wrapper's test that keeps C from aliasing A or B: exact on
+    rows, so C may live in the padding columns of A; checked against a
+    brute-force set intersection of element addresses."""
+    torch = pytest.importorskip("torch")
+    import itertools
+
+    import numpy as np
+
+    buf = torch.zeros(1000)
+    a = buf[:400].view(20, 20)
+    assert mg._overlaps(a, a)
+    assert mg._overlaps(a, buf[399:400].view(1, 1))            # last element shared
+    assert not mg._overlaps(a, buf[400:800].view(20, 20))      # adjacent, disjoint
+    strided = a[:, :5]                                          # rows of 5 at stride 20
+    assert mg._overlaps(strided, buf[383:388].view(1, 5))
+    assert not mg._overlaps(strided, buf[385:390].view(1, 5))   # past the last row
+    assert not mg._overlaps(strided, a[:, 5:20])                # the padding columns
+    assert not mg._overlaps(strided, a[:, 5:20][:, :0])         # empty
+
+    def addrs(t):
+        return {t.data_ptr() + 4 * (i * t.stride(0) + j) for i in range(t.shape[0]) for j in range(t.shape[1])}
+
+    rng = np.random.default_rng(7)
+    views = []
+    for _ in range(60):
+        r, c = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        ld = c + int(rng.integers(0, 4))
+        off = int(rng.integers(0, 60))
+        views.append(buf[off:off + r * ld].view(r, ld)[:, :c])
+    for x, y in itertools.combinations(views, 2):
+        assert mg._overlaps(x, y) == bool(addrs(x) & addrs(y))
