@@ -15,7 +15,9 @@
 //   * Each wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of C held in
 //     accumulator registers as FM x FN blocks of 32 x 32 (the register tile of
 //     the same page, section 3.4, moved onto the matrix cores), and issues
-//     v_mfma_f32_32x32x2_f32: full FP32 inputs, products and sums.
+//     v_mfma_f32_32x32x2_f32: full FP32 inputs, products and sums. MI16
+//     configurations hold 16 x 16 blocks instead and issue
+//     v_mfma_f32_16x16x4_f32 (see Frag16).
 //   * k-permutation: inside a k-tile, the two 32-lane halves of a wave feed the
 //     MFMA's two k slots from the two halves of the tile (slot h of step s is
 //     k = h*BK/2 + s). Any permutation of k applied to both operands only
@@ -62,6 +64,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "misgemm.h"
@@ -105,8 +108,17 @@ struct GemmArgs {
 // groups of waves take alternate k-tiles (split-K inside the workgroup), each
 // with its own LDS buffers, and are summed at the end in group order.
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KG_ = 1, int EU_ = 0, bool SPLIT_ = false,
-          bool STREAMK_ = false, bool DL_ = false>
+          bool STREAMK_ = false, bool DL_ = false, bool MI16_ = false>
 struct TileCfg {
+    // MI16: blocks of 16 x 16 on v_mfma_f32_16x16x4_f32 (four accumulator
+    // registers each, 16-deep q-groups) instead of 32 x 32 on
+    // v_mfma_f32_32x32x2_f32 (sixteen registers, 8-deep q-groups). At one
+    // wave per SIMD a small wave tile runs faster as 16 x 16 blocks (64 x 64
+    // tile at 1024^3: 22.6 vs 27.5 us).
+    static constexpr bool MI16 = MI16_;
+    static constexpr int MBLK = MI16 ? 16 : 32;      // block edge
+    static constexpr int ACC_REGS = MI16 ? 4 : 16;   // accumulator registers per block
+    static constexpr int QK = MI16 ? 16 : 8;         // k per q-group
     // DL: the straight-line rounds move tiles global -> LDS directly
     // (global_load_lds_dwordx4), with unpadded, chunk-swizzled LDS rows.
     static constexpr bool DL = DL_;
@@ -120,13 +132,13 @@ struct TileCfg {
     static constexpr int NTG = 64 * WAVES_M * WAVES_N;   // threads per k-group
     static constexpr int NT = NTG * KG;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    static constexpr int FM = WTM / 32, FN = WTN / 32;
+    static constexpr int FM = WTM / MBLK, FN = WTN / MBLK;
     // Waves per SIMD the register allocation must allow: at least two (two
     // workgroups per CU where LDS allows), more when one workgroup alone
     // places more than two waves on each SIMD.
     static constexpr int WAVES_PER_EU = EU_ ? EU_ : (NT / 256 > 2 ? NT / 256 : 2);
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    static_assert(WTM % MBLK == 0 && WTN % MBLK == 0, "wave tile must be whole blocks");
+    static_assert(BK % (2 * QK) == 0, "fragment buffers alternate, so a k-tile holds an even number of q-groups");
 };
 
 // n adjacent floats from LDS (n = 1, 2, 4), as one ds_read.
@@ -365,6 +377,75 @@ struct Frag {
     }
 };
 
+// MFMA operands of one 16-deep q-group for one wave on 16 x 16 blocks:
+// a[blk][s] and b[blk][s] feed step s of v_mfma_f32_16x16x4_f32. Lane (c, g)
+// = (lane % 16, lane / 16) supplies row / column c of a block and, at step s,
+// k = 16q + 4g + s (a k-permutation shared by both operands): one 16-byte
+// read gives a k-contiguous operand's four steps. m/n-contiguous operands
+// use the column permutation m = FM*c + block (n = FN*c + block), one read of
+// FM (FN) adjacent floats per step.
+template <class CFG, bool TA, bool TB>
+struct Frag16 {
+    static constexpr int FM = CFG::FM, FN = CFG::FN, WTM = CFG::WTM, WTN = CFG::WTN;
+    static_assert(!TA || FM == 1 || FM == 2 || FM == 4, "one LDS read covers a row's FM blocks");
+    static_assert(TB || FN == 1 || FN == 2 || FN == 4, "one LDS read covers a row's FN blocks");
+    float a[FM][4];
+    float b[FN][4];
+
+    // Float offset of the lane's four k values inside a k-contiguous LDS row
+    // (row c plus a multiple of 16), at its swizzled chunk position in the DL
+    // layout.
+    static __device__ __forceinline__ int kofs(int c, int g, int q) {
+        if constexpr (CFG::DL) {
+            return ((4 * q + g) ^ (c & 7)) * 4;
+        } else {
+            return 16 * q + 4 * g;
+        }
+    }
+
+    // c, g: the lane's column and group (lane % 16, lane / 16).
+    template <int AS, int BS>
+    __device__ __forceinline__ void read(const float *as, const float *bs, int q, int wm, int wn, int c, int g) {
+        const int k0 = 16 * q + 4 * g;
+        if (!TA) {
+#pragma unroll
+            for (int blk = 0; blk < FM; ++blk)
+                LdsVec<4>::get(as + (wm * WTM + 16 * blk + c) * AS + kofs(c, g, q), a[blk]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                float t[FM];
+                LdsVec<FM>::get(as + (k0 + s) * AS + wm * WTM + FM * c, t);
+#pragma unroll
+                for (int blk = 0; blk < FM; ++blk) a[blk][s] = t[blk];
+            }
+        }
+        if (TB) {
+#pragma unroll
+            for (int blk = 0; blk < FN; ++blk)
+                LdsVec<4>::get(bs + (wn * WTN + 16 * blk + c) * BS + kofs(c, g, q), b[blk]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                float t[FN];
+                LdsVec<FN>::get(bs + (k0 + s) * BS + wn * WTN + FN * c, t);
+#pragma unroll
+                for (int blk = 0; blk < FN; ++blk) b[blk][s] = t[blk];
+            }
+        }
+    }
+
+    __device__ __forceinline__ void mma(f32x4 (&acc)[FM][FN]) const {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+    }
+};
+
 // Instruction-order hints for the straight-line k-tile iteration (one
 // scheduling region ending at the barrier): the next tile's global loads are
 // spread over the first MFMAs, each q-group's fragment reads for the next
@@ -420,19 +501,21 @@ __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(CFG::WA
 void sgemm_mfma32(GemmArgs g) {
     constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NTG = CFG::NTG, KG = CFG::KG;
     constexpr int FM = CFG::FM, FN = CFG::FN, WTM = CFG::WTM, WTN = CFG::WTN;
-    constexpr int Q = BK / 8;                   // q-groups per k-tile
+    constexpr int Q = BK / CFG::QK;             // q-groups per k-tile
+    constexpr int AR = CFG::ACC_REGS, MBLK = CFG::MBLK;
+    using AccT = std::conditional_t<CFG::MI16, f32x4, f32x16>;
     static_assert(Q % 2 == 0, "fragment buffers alternate, so the q-group count must be even");
     // Stored tile shapes: A is BM x BK ('N', k contiguous) or BK x BM ('T',
     // m contiguous); B is BK x BN ('N', n contiguous) or BN x BK ('T').
     using ACopy = TileCopy<TA ? BK : BM, TA ? BM : BK, NTG, CFG::DL, CFG::DL && !TA>;
     using BCopy = TileCopy<TB ? BN : BK, TB ? BK : BN, NTG, CFG::DL, CFG::DL && TB>;
-    using F = Frag<CFG, TA, TB>;
+    using F = std::conditional_t<CFG::MI16, Frag16<CFG, TA, TB>, Frag<CFG, TA, TB>>;
     constexpr int A_FLOATS = ACopy::LDS_FLOATS, B_FLOATS = BCopy::LDS_FLOATS;
     constexpr int AS = ACopy::STRIDE, BS = BCopy::STRIDE;
     constexpr int GROUP_FLOATS = 2 * (A_FLOATS + B_FLOATS);
     // The k-group reduction reuses the tile buffers: KG-1 groups x waves x
     // FM*FN accumulator blocks x 16 registers x 64 lanes.
-    constexpr int RED_FLOATS = (KG - 1) * (NTG / 64) * FM * FN * 16 * 64;
+    constexpr int RED_FLOATS = (KG - 1) * (NTG / 64) * FM * FN * AR * 64;
     static_assert(RED_FLOATS <= KG * GROUP_FLOATS, "reduction does not fit the tile buffers");
 
     __shared__ __attribute__((aligned(16))) float lds[KG * GROUP_FLOATS];
@@ -453,7 +536,9 @@ void sgemm_mfma32(GemmArgs g) {
         const int grp = KG == 1 ? 0 : tid / NTG;    // k-group
         const int gtid = KG == 1 ? tid : tid % NTG;  // thread within it
         const int lane = gtid & 63, wave = gtid >> 6;
-        const int li = lane & 31, lh = lane >> 5;
+        // Lane column and group: (lane % 32, lane / 32) for 32 x 32 blocks,
+        // (lane % 16, lane / 16) for 16 x 16 blocks.
+        const int li = CFG::MI16 ? (lane & 15) : (lane & 31), lh = CFG::MI16 ? (lane >> 4) : (lane >> 5);
         const int wm = wave / CFG::WAVES_N, wn = wave % CFG::WAVES_N;
         // This group's buffer i of A at a_lds + i*A_FLOATS, of B at b_lds + i*B_FLOATS.
         float *const a_lds = lds + grp * GROUP_FLOATS;
@@ -491,13 +576,13 @@ void sgemm_mfma32(GemmArgs g) {
                     guard, vec, gtid);
         };
 
-        f32x16 acc[FM][FN];
+        AccT acc[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                for (int r = 0; r < AR; ++r) acc[i][j][r] = 0.0f;
 
         F f0, f1;
         // Group grp takes k-tiles kt_begin + grp, + KG, ... In round r its k-tile
@@ -586,7 +671,7 @@ void sgemm_mfma32(GemmArgs g) {
             // Groups 1..KG-1 hand their accumulators to group 0 through LDS (the
             // tile buffers are free after the last barrier); group 0 adds them in
             // group order, so the sum is the same on every call.
-            constexpr int SLOT = FM * FN * 16 * 64;            // floats per wave
+            constexpr int SLOT = FM * FN * AR * 64;            // floats per wave
             constexpr int WAVES = NTG / 64;
             if (grp > 0) {
                 float *dst = lds + ((grp - 1) * WAVES + wave) * SLOT + lane;
@@ -595,7 +680,7 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) dst[((i * FN + j) * 16 + r) * 64] = acc[i][j][r];
+                        for (int r = 0; r < AR; ++r) dst[((i * FN + j) * AR + r) * 64] = acc[i][j][r];
             }
             __syncthreads();
             // Without split-K no barrier follows, so the other groups are done.
@@ -609,7 +694,7 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * FN + j) * 16 + r) * 64];
+                        for (int r = 0; r < AR; ++r) acc[i][j][r] += src[((i * FN + j) * AR + r) * 64];
             }
         }
 
@@ -619,7 +704,7 @@ void sgemm_mfma32(GemmArgs g) {
             // stores, count in, and let the workgroup that completes the count sum
             // the partials in split order before the epilogue. Same protocol as the
             // skinny band kernel; every wave of the workgroup reaches each barrier.
-            constexpr int REGS = FM * FN * 16;
+            constexpr int REGS = FM * FN * AR;
             constexpr size_t PART = (size_t)BM * BN;
             const int S = sg.nseg;
             const size_t tile_id = (size_t)sg.counter;
@@ -630,8 +715,8 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < FN; ++j)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            __hip_atomic_store(mine + ((i * FN + j) * 16 + r) * 64, acc[i][j][r], __ATOMIC_RELAXED,
+                        for (int r = 0; r < AR; ++r)
+                            __hip_atomic_store(mine + ((i * FN + j) * AR + r) * 64, acc[i][j][r], __ATOMIC_RELAXED,
                                                kExchangeScope);
             }
             __builtin_amdgcn_s_waitcnt(0);
@@ -647,12 +732,12 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                    for (int r = 0; r < AR; ++r) acc[i][j][r] = 0.0f;
             // SB splits' loads in flight at a time (about 64 registers); the sum
             // runs in split order.
             constexpr int SB = (REGS >= 64 || CFG::WAVES_PER_EU > 2) ? 1 : 64 / REGS;
             for (int sp0 = 0; sp0 < S; sp0 += SB) {
-                float v[SB][FM][FN][16];
+                float v[SB][FM][FN][AR];
 #pragma unroll
                 for (int u = 0; u < SB; ++u)
 #pragma unroll
@@ -660,10 +745,10 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r)
+                            for (int r = 0; r < AR; ++r)
                                 v[u][i][j][r] = (grp == 0 && sp0 + u < S)
                                                     ? __hip_atomic_load(base + (size_t)sg.slot(sp0 + u) * PART +
-                                                                            ((i * FN + j) * 16 + r) * 64,
+                                                                            ((i * FN + j) * AR + r) * 64,
                                                                         __ATOMIC_RELAXED, kExchangeScope)
                                                     : 0.0f;
 #pragma unroll
@@ -674,14 +759,15 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
                             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                                for (int r = 0; r < 16; ++r) acc[i][j][r] += v[u][i][j][r];
+                                for (int r = 0; r < AR; ++r) acc[i][j][r] += v[u][i][j][r];
             }
             if (tid == 0) __hip_atomic_store(&g.counters[tile_id], 0, __ATOMIC_RELAXED, kExchangeScope);
         }
         if (grp > 0) return;
 
         // Epilogue. Accumulator element r of block (i, j) in lane (li, lh) is
-        // block row 8*(r/4) + 4*lh + r%4, block column li.
+        // block row 8*(r/4) + 4*lh + r%4 (32 x 32 blocks) or 4*lh + r (16 x 16
+        // blocks), block column li.
         const float alpha = g.alpha, beta = g.beta;
         float *const cw = g.C + (size_t)(m0 + wm * WTM) * g.ldc + (n0 + wn * WTN);
         const int rows_left = M - (m0 + wm * WTM), cols_left = N - (n0 + wn * WTN);
@@ -689,9 +775,9 @@ void sgemm_mfma32(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ib = 8 * (r / 4) + 4 * lh + (r % 4);
-                const int row = TA ? FM * ib + i : 32 * i + ib;
+            for (int r = 0; r < AR; ++r) {
+                const int ib = CFG::MI16 ? 4 * lh + r : 8 * (r / 4) + 4 * lh + (r % 4);
+                const int row = TA ? FM * ib + i : MBLK * i + ib;
                 if (row >= rows_left) continue;
                 float *crow = cw + (size_t)row * ldc;
                 if (!TB) {
@@ -704,7 +790,7 @@ void sgemm_mfma32(GemmArgs g) {
                 } else {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
-                        const int col = 32 * j + li;
+                        const int col = MBLK * j + li;
                         if (col < cols_left) {
                             float *p = crow + col;
                             const float o = alpha * acc[i][j][r];
@@ -1268,6 +1354,17 @@ using CfgTS = TileCfg<128, 256, 32, 2, 4, 1, 0, false, true>;
 // Direct global -> LDS loads in the straight-line rounds.
 using CfgQ32D = TileCfg<256, 256, 32, 4, 2, 1, 0, false, false, true>;
 using CfgL42D = TileCfg<128, 128, 32, 4, 2, 1, 4, false, false, true>;
+// 16 x 16 MFMA blocks.
+using Cfg16S = TileCfg<64, 64, 32, 2, 2, 1, 0, false, false, false, true>;
+using Cfg16S2 = TileCfg<64, 64, 32, 2, 2, 2, 0, false, false, false, true>;
+using Cfg16S4 = TileCfg<64, 64, 32, 2, 2, 4, 0, false, false, false, true>;
+using Cfg16SK = TileCfg<64, 64, 32, 2, 2, 1, 0, true, false, false, true>;
+using Cfg16L42 = TileCfg<128, 128, 32, 4, 2, 1, 4, false, false, false, true>;
+using Cfg16L42S1 = TileCfg<128, 128, 32, 4, 2, 1, 2, false, true, false, true>;
+using Cfg16L = TileCfg<128, 128, 32, 2, 2, 1, 0, false, false, false, true>;
+using Cfg16W = TileCfg<256, 128, 32, 4, 2, 1, 0, false, false, false, true>;
+using Cfg16L42D = TileCfg<128, 128, 32, 4, 2, 1, 4, false, false, true, true>;
+using Cfg16S4D = TileCfg<64, 64, 32, 2, 2, 4, 0, false, false, true, true>;
 
 // Config ids: the index of each entry of kConfigs below.
 enum ConfigId : int {
@@ -1296,6 +1393,16 @@ enum ConfigId : int {
     kCfgLadderLast = kCfgLadderFirst + misgemm_ladder::kNumRungs - 1,
     kCfg256x256Dl = 25,
     kCfg128W42Dl = 26,
+    kCfg16x64 = 27,
+    kCfg16x64Kg2 = 28,
+    kCfg16x64Kg4 = 29,
+    kCfg16x64Split = 30,
+    kCfg16x128W42 = 31,
+    kCfg16StreamK1 = 32,
+    kCfg16x128 = 33,
+    kCfg16x256x128 = 34,
+    kCfg16x128W42Dl = 35,
+    kCfg16x64Kg4Dl = 36,
 };
 
 struct ConfigInfo {
@@ -1331,10 +1438,20 @@ constexpr ConfigInfo kConfigs[] = {
     {"valu_vec2d_128x128x8_8x8_dbuf", 128, 128, 256},
     {"mfma32_256x256x32_w4x2_dl", CfgQ32D::BM, CfgQ32D::BN, CfgQ32D::NT},
     {"mfma32_128x128x32_w4x2_dl", CfgL42D::BM, CfgL42D::BN, CfgL42D::NT},
+    {"mfma16_64x64x32_w2x2", Cfg16S::BM, Cfg16S::BN, Cfg16S::NT},
+    {"mfma16_64x64x32_w2x2_kg2", Cfg16S2::BM, Cfg16S2::BN, Cfg16S2::NT},
+    {"mfma16_64x64x32_w2x2_kg4", Cfg16S4::BM, Cfg16S4::BN, Cfg16S4::NT},
+    {"mfma16_64x64x32_w2x2_splitk", Cfg16SK::BM, Cfg16SK::BN, Cfg16SK::NT},
+    {"mfma16_128x128x32_w4x2", Cfg16L42::BM, Cfg16L42::BN, Cfg16L42::NT},
+    {"mfma16_128x128x32_w4x2_streamk_1wg", Cfg16L42S1::BM, Cfg16L42S1::BN, Cfg16L42S1::NT},
+    {"mfma16_128x128x32_w2x2", Cfg16L::BM, Cfg16L::BN, Cfg16L::NT},
+    {"mfma16_256x128x32_w4x2", Cfg16W::BM, Cfg16W::BN, Cfg16W::NT},
+    {"mfma16_128x128x32_w4x2_dl", Cfg16L42D::BM, Cfg16L42D::BN, Cfg16L42D::NT},
+    {"mfma16_64x64x32_w2x2_kg4_dl", Cfg16S4D::BM, Cfg16S4D::BN, Cfg16S4D::NT},
 };
 constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-static_assert(kNumConfigs == kCfg128W42Dl + 1, "one ConfigId per kConfigs entry");
+static_assert(kNumConfigs == kCfg16x64Kg4Dl + 1, "one ConfigId per kConfigs entry");
 static_assert(kCfgLadderLast + 1 == kCfg256x256Dl, "the ladder ids are contiguous");
 static_assert(kConfigs[kCfg128].bm == CfgL::BM && kConfigs[kCfg128].bn == CfgL::BN && kConfigs[kCfg128].nt == CfgL::NT, "kConfigs order");
 static_assert(kConfigs[kCfg64].bm == CfgS::BM && kConfigs[kCfg64].bn == CfgS::BN && kConfigs[kCfg64].nt == CfgS::NT, "kConfigs order");
@@ -1457,6 +1574,8 @@ long long splits_64x64(long long tiles, int ktiles) {
 //                       over workgroups when those would fill under 75% of
 //                       the CU slots; <= 256 four k-groups or split-K,
 //                       whichever the 64 x 64 timing model puts first.
+// The 128 x 128 (8 waves), one-workgroup stream-K 128 x 128 and 64 x 64
+// tiles run as 16 x 16 MFMA blocks; the larger tiles as 32 x 32 blocks.
 int select_config(char transA, char transB, int M, int N, int K) {
     // Few rows: the band kernel streams op(B) once; below one 128-column band
     // its padding costs more than a tile kernel (32 x 64 x 64: 8.9 vs 5.6 us).
@@ -1465,16 +1584,17 @@ int select_config(char transA, char transB, int M, int N, int K) {
     const long long t128 = tiles(128, 128), t64 = tiles(64, 64);
     // Stream-K work: 128 x 128 x 32 iterations.
     const long long sk_iters = t128 * ((K + 31) / 32);
-    // The 128 x 128 tile with only A transposed loads directly into LDS:
-    // 5-20% faster there (2048^3 TN: 129 vs 154 us), 1-3% slower elsewhere.
-    const int cfg128 = op_t(transA) && op_n(transB) ? kCfg128W42Dl : kCfg128W42;
+    // The 128 x 128 and 64 x 64 tiles run as 16 x 16 MFMA blocks, 2-18%
+    // faster than as 32 x 32 blocks for every op pair (1024^3: 22 vs 24 us;
+    // 2048 x 4096 x 1024 TN: 132 vs 144 us).
+    const int cfg128 = kCfg16x128W42;
     if (t128 >= kNumCus) {
         const bool ta = op_t(transA), tb = op_t(transB);
         // Big tiles (one workgroup per CU) lose to 128 x 128 (two per CU)
-        // when K is short and the grid fills the chip only once, except with
-        // only A transposed; with both transposed, 256 x 128 is the one that
-        // gains (the 256 x 256 and 128 x 256 x 16 tiles do not).
-        const bool big_ok = !(K < 2048 && t128 < 4 * kNumCus) || (ta && !tb);
+        // when K is short and the grid fills the chip only once; with both
+        // transposed, 256 x 128 is the one that gains (the register-staged
+        // 256 x 256 and 128 x 256 x 16 tiles do not).
+        const bool big_ok = !(K < 2048 && t128 < 4 * kNumCus);
         const bool tt = ta && tb;
         const bool wide = !tt && M < N;    // 128 x 256 rather than 256 x 128
         // With both transposed, the 256 x 256 tile with direct-to-LDS loads
@@ -1494,22 +1614,22 @@ int select_config(char transA, char transB, int M, int N, int K) {
         if (best == s_sk) return kCfgStreamK2;
         if (best == s_b4) return kCfg128x256x16;
         if (best == s_b8) return wide ? kCfg128x256 : kCfg256x128;
-        return best == s_128 ? cfg128 : kCfg64;
+        return best == s_128 ? cfg128 : kCfg16x64;
     }
     // 144..255 tiles of 128 x 128 with at least 20 k-tiles per workgroup:
     // stream-K, one workgroup per CU.
-    if (t128 >= 144 && sk_iters >= 20LL * kNumCus) return kCfgStreamK1;
+    if (t128 >= 144 && sk_iters >= 20LL * kNumCus) return kCfg16StreamK1;
     if (t128 >= 3 * kNumCus / 4) return cfg128;
-    if (t64 >= 2 * kNumCus) return kCfg64;
+    if (t64 >= 2 * kNumCus) return kCfg16x64;
     // 257..511 tiles of 64 x 64: two k-groups unless their workgroups would
     // leave the CU slots badly filled; then split-K over workgroups, whose
     // smaller workgroups spread more evenly.
-    if (t64 > kNumCus) return (double)t64 / (2 * kNumCus) >= 0.75 ? kCfg64Kg2 : kCfg64Split;
+    if (t64 > kNumCus) return (double)t64 / (2 * kNumCus) >= 0.75 ? kCfg16x64Kg2 : kCfg16x64Split;
     // Up to 256 tiles of 64 x 64: four k-groups or split-K over workgroups,
     // whichever the timing model puts first.
     const int ktiles = (K + 31) / 32;
     const double t_split = model_64x64_us(t64, ktiles, 1, splits_64x64(t64, ktiles));
-    return t_split < model_64x64_us(t64, ktiles, 4, 1) ? kCfg64Split : kCfg64Kg4;
+    return t_split < model_64x64_us(t64, ktiles, 4, 1) ? kCfg16x64Split : kCfg16x64Kg4;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -1837,6 +1957,16 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case kCfgStreamK256x128: err = launch_cfg<CfgWS>(ta, tb, g, stream); break;
         case kCfg256x256Dl: err = launch_cfg<CfgQ32D>(ta, tb, g, stream); break;
         case kCfg128W42Dl: err = launch_cfg<CfgL42D>(ta, tb, g, stream); break;
+        case kCfg16x64: err = launch_cfg<Cfg16S>(ta, tb, g, stream); break;
+        case kCfg16x64Kg2: err = launch_cfg<Cfg16S2>(ta, tb, g, stream); break;
+        case kCfg16x64Kg4: err = launch_cfg<Cfg16S4>(ta, tb, g, stream); break;
+        case kCfg16x64Split: err = launch_cfg<Cfg16SK>(ta, tb, g, stream, 2); break;
+        case kCfg16x128W42: err = launch_cfg<Cfg16L42>(ta, tb, g, stream); break;
+        case kCfg16StreamK1: err = launch_cfg<Cfg16L42S1>(ta, tb, g, stream); break;
+        case kCfg16x128: err = launch_cfg<Cfg16L>(ta, tb, g, stream); break;
+        case kCfg16x256x128: err = launch_cfg<Cfg16W>(ta, tb, g, stream); break;
+        case kCfg16x128W42Dl: err = launch_cfg<Cfg16L42D>(ta, tb, g, stream); break;
+        case kCfg16x64Kg4Dl: err = launch_cfg<Cfg16S4D>(ta, tb, g, stream); break;
         default: err = launch_cfg<CfgTS>(ta, tb, g, stream); break;   // kCfgStreamK128x256
     }
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;

@@ -117,42 +117,42 @@ def test_shape_class_selection():
     assert sel("T", "T", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2_dl"
     assert sel("T", "T", 4096, 4096, 1024) == "mfma32_256x256x32_w4x2_dl"
     assert sel("T", "T", 2048, 4096, 2048) == "mfma32_256x128x32_w4x2"
-    # Only A transposed: the 128 x 128 tile loads directly into LDS.
-    assert sel("T", "N", 2048, 2048, 2048) == "mfma32_128x128x32_w4x2_dl"
-    assert sel("T", "N", 2048, 2048, 4096) == "mfma32_128x128x32_w4x2_dl"
-    assert sel("N", "N", 2048, 2048, 2048) == "mfma32_128x128x32_w4x2"
+    # 128 x 128 and 64 x 64 tiles run as 16 x 16 MFMA blocks, for every op pair.
+    assert sel("T", "N", 2048, 2048, 2048) == "mfma16_128x128x32_w4x2"
+    assert sel("T", "N", 2048, 2048, 4096) == "mfma16_128x128x32_w4x2"
+    assert sel("N", "N", 2048, 2048, 2048) == "mfma16_128x128x32_w4x2"
     # 2048 x 4096 x 1024: short K on a grid that fills the chip once: 128 x 128
-    # (two workgroups per CU), except with only A transposed.
-    assert sel("N", "N", 2048, 4096, 1024) == "mfma32_128x128x32_w4x2"
-    assert sel("T", "N", 2048, 4096, 1024) == "mfma32_128x256x32_w2x4"
+    # (two workgroups per CU), for every op pair.
+    assert sel("N", "N", 2048, 4096, 1024) == "mfma16_128x128x32_w4x2"
+    assert sel("T", "N", 2048, 4096, 1024) == "mfma16_128x128x32_w4x2"
     assert sel("N", "N", 2048, 4096, 2048) == "mfma32_128x256x32_w2x4"
-    assert sel("T", "T", 2048, 4096, 1024) == "mfma32_128x128x32_w4x2"
-    assert sel("N", "T", 2048, 4096, 1024) == "mfma32_128x128x32_w4x2"
+    assert sel("T", "T", 2048, 4096, 1024) == "mfma16_128x128x32_w4x2"
+    assert sel("N", "T", 2048, 4096, 1024) == "mfma16_128x128x32_w4x2"
     # 1024^2 output: 64 tiles of 128 x 128 only, so smaller tiles with four k-groups.
-    assert sel("N", "N", 1024, 1024, 1024) == "mfma32_64x64x32_w2x2_kg4"
-    assert sel("N", "N", 1000, 1300, 700) == "mfma32_64x64x32_w2x2_splitk"
-    assert sel("N", "N", 1280, 1280, 1280) == "mfma32_64x64x32_w2x2_kg2"
-    assert sel("N", "N", 512, 512, 512) == "mfma32_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 1024, 1024, 1024) == "mfma16_64x64x32_w2x2_kg4"
+    assert sel("N", "N", 1000, 1300, 700) == "mfma16_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 1280, 1280, 1280) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 512, 512, 512) == "mfma16_64x64x32_w2x2_splitk"
     # Up to 256 tiles of 64 x 64: split-K where the 64 x 64 timing model puts
     # it ahead of four k-groups (short grids, long K).
-    assert sel("N", "N", 768, 768, 768) == "mfma32_64x64x32_w2x2_splitk"
-    assert sel("T", "T", 832, 832, 832) == "mfma32_64x64x32_w2x2_splitk"
-    assert sel("N", "N", 2048, 256, 2048) == "mfma32_64x64x32_w2x2_splitk"
-    assert sel("N", "N", 960, 960, 960) == "mfma32_64x64x32_w2x2_kg4"
+    assert sel("N", "N", 768, 768, 768) == "mfma16_64x64x32_w2x2_splitk"
+    assert sel("T", "T", 832, 832, 832) == "mfma16_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 2048, 256, 2048) == "mfma16_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 960, 960, 960) == "mfma16_64x64x32_w2x2_kg4"
     # 361 tiles fill under 75% of two slots per CU: split-K.
-    assert sel("N", "N", 1216, 1216, 1216) == "mfma32_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 1216, 1216, 1216) == "mfma16_64x64x32_w2x2_splitk"
     # 144..255 tiles of 128 x 128 with enough k-work: stream-K, one workgroup per CU.
-    assert sel("N", "N", 1792, 1792, 1792) == "mfma32_128x128x32_w4x2_streamk_1wg"
-    assert sel("N", "N", 1536, 1536, 1536) == "mfma32_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "N", 1792, 1792, 1792) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "N", 1536, 1536, 1536) == "mfma16_128x128x32_w4x2_streamk_1wg"
     # ... but not with little k-work per workgroup.
-    assert sel("N", "N", 1536, 1536, 256) == "mfma32_64x64x32_w2x2"
+    assert sel("N", "N", 1536, 1536, 256) == "mfma16_64x64x32_w2x2"
     # Square sizes: whichever tile spreads most evenly over the 256 CUs.
     # Stream-K over 256 x 128 tiles where no data-parallel tile spreads evenly.
-    skw = "256x128x32_w4x2_streamk"
-    for n, want in [(2048, "128x128x32_w4x2"), (2304, skw), (2560, skw), (2816, "256x128x32_w4x2"), (3072, skw),
-                    (3328, skw), (3584, skw), (3840, skw), (4096, "256x256x32_w4x2"),
-                    (8192, "256x256x32_w4x2")]:
-        assert sel("N", "N", n, n, n) == "mfma32_" + want, n
+    skw = "mfma32_256x128x32_w4x2_streamk"
+    for n, want in [(2048, "mfma16_128x128x32_w4x2"), (2304, skw), (2560, skw), (2816, "mfma32_256x128x32_w4x2"),
+                    (3072, skw), (3328, skw), (3584, skw), (3840, skw), (4096, "mfma32_256x256x32_w4x2"),
+                    (8192, "mfma32_256x256x32_w4x2")]:
+        assert sel("N", "N", n, n, n) == want, n
     # Stream-K over big tiles for the transposed op pairs too; 128 x 128 (two
     # per CU) where big tiles do not pay.
     assert sel("N", "T", 3072, 3072, 3072) == "mfma32_256x128x32_w4x2_streamk"
