@@ -166,7 +166,8 @@ template <> struct LdsVec<4> {
 // DL layout (for direct global -> LDS loads, which write a wave's 64 chunks
 // to 1 KB of consecutive LDS): rows are unpadded, [R][CC]. When SWZ (a
 // k-contiguous tile, read as 16-byte runs down 8 consecutive rows), chunk c
-// of row r sits at chunk position c ^ swz(r), so those 8 reads fall on 8
+// of row r sits at chunk position c ^ swz(r) -- r mod 8 for rows of 8 or
+// more chunks, (r / 2) mod 4 for rows of 4 -- so those 8 reads fall on 8
 // different 16-byte bank groups, as the padding achieves otherwise.
 template <int R, int CC, int NT, bool DL = false, bool SWZ = false>
 struct TileCopy {
@@ -176,11 +177,11 @@ struct TileCopy {
     static constexpr int STRIDE = DL ? CC : CC + kLdsPad;
     static constexpr int LDS_FLOATS = R * STRIDE;
     static_assert(CC % 4 == 0 && CHUNKS % NT == 0, "tile must split evenly over the threads");
-    static_assert(!SWZ || (DL && (CPR == 4 || CPR == 8)), "swizzle is for 16- or 32-wide k-contiguous rows");
+    static_assert(!SWZ || (DL && (CPR == 4 || CPR % 8 == 0)), "swizzle is for 16-wide or multiple-of-32-wide k-contiguous rows");
     static_assert(!DL || NT % 64 == 0, "direct loads are issued per wave");
 
     // Chunk position of chunk c in row r (SWZ), and its LDS float offset.
-    static __device__ __forceinline__ int swz(int r) { return SWZ ? (r / (8 / CPR)) & (CPR - 1) : 0; }
+    static __device__ __forceinline__ int swz(int r) { return SWZ ? (CPR >= 8 ? r & 7 : (r / 2) & 3) : 0; }
     static __device__ __forceinline__ int at(int r, int c) { return r * STRIDE + ((c / 4) ^ swz(r)) * 4; }
 
     f32x4 v[PER_THREAD];
@@ -325,7 +326,7 @@ struct Frag {
     static __device__ __forceinline__ int kofs(int li, int lh, int q) {
         if constexpr (CFG::DL) {
             constexpr int CPR = CFG::BK / 4;
-            return (((lh * HB + 4 * q) / 4) ^ ((li / (8 / CPR)) & (CPR - 1))) * 4;
+            return (((lh * HB + 4 * q) / 4) ^ (CPR >= 8 ? li & 7 : (li / 2) & 3)) * 4;
         } else {
             return lh * HB + 4 * q;
         }
@@ -1559,6 +1560,8 @@ long long splits_64x64(long long tiles, int ktiles) {
 //                         per CU (B not transposed)          0.955 (always balanced)
 //                       stream-K 128 x 128, two workgroups per CU
 //                         (either: >= 8 k-tiles per workgroup) 0.925 (always balanced)
+//                       stream-K 128 x 128 of 16 x 16 blocks, one
+//                         workgroup per CU (neither transposed) 0.965 (always balanced)
 //                       128 x 256 with 4 waves (two workgroups per CU; B
 //                         not transposed)                    1.038 x balance over 2 slots per CU
 //                       256 x 128 / 128 x 256 with 8 waves (one per CU; B
@@ -1608,8 +1611,14 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const bool sk_ok = sk_iters >= 8LL * 2 * kNumCus;
         const double s_skb = (sk_ok && big_ok) ? 0.955 : -1.0;
         const double s_sk = sk_ok ? 0.925 : -1.0;
-        const double best = fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(s_128, s_64));
+        // With neither operand transposed, stream-K over 128 x 128 tiles of
+        // 16 x 16 blocks, one workgroup per CU, beats the big-tile stream-K
+        // (n = 2304: 193 vs 202 us; 3840: 839 vs 854).
+        const double s_sk16 = (sk_ok && !ta && !tb) ? 0.965 : -1.0;
+        const double best =
+            fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(fmax(s_128, s_64), s_sk16));
         if (best == s_q) return tt ? kCfg256x256Dl : kCfg256x256;
+        if (best == s_sk16) return kCfg16StreamK1;
         if (best == s_skb) return wide ? kCfgStreamK128x256 : kCfgStreamK256x128;
         if (best == s_sk) return kCfgStreamK2;
         if (best == s_b4) return kCfg128x256x16;

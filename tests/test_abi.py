@@ -149,8 +149,9 @@ def test_shape_class_selection():
     # Square sizes: whichever tile spreads most evenly over the 256 CUs.
     # Stream-K over 256 x 128 tiles where no data-parallel tile spreads evenly.
     skw = "mfma32_256x128x32_w4x2_streamk"
-    for n, want in [(2048, "mfma16_128x128x32_w4x2"), (2304, skw), (2560, skw), (2816, "mfma32_256x128x32_w4x2"),
-                    (3072, skw), (3328, skw), (3584, skw), (3840, skw), (4096, "mfma32_256x256x32_w4x2"),
+    sk16 = "mfma16_128x128x32_w4x2_streamk_1wg"
+    for n, want in [(2048, "mfma16_128x128x32_w4x2"), (2304, sk16), (2560, sk16), (2816, "mfma32_256x128x32_w4x2"),
+                    (3072, sk16), (3328, sk16), (3584, sk16), (3840, sk16), (4096, "mfma32_256x256x32_w4x2"),
                     (8192, "mfma32_256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == want, n
     # Stream-K over big tiles for the transposed op pairs too; 128 x 128 (two
@@ -158,8 +159,9 @@ def test_shape_class_selection():
     assert sel("N", "T", 3072, 3072, 3072) == "mfma32_256x128x32_w4x2_streamk"
     assert sel("T", "T", 2560, 2560, 2560) == "mfma32_256x128x32_w4x2_streamk"
     assert sel("N", "T", 2304, 2304, 1024) == "mfma32_128x128x32_w4x2_streamk_2wg"
-    # N > M: the 128 x 256 stream-K tile.
-    assert sel("N", "N", 2304, 3328, 2048) == "mfma32_128x256x32_w2x4_streamk"
+    # N > M: NN takes the 16 x 16 stream-K tile; transposed B keeps the 128 x 256 stream-K tile.
+    assert sel("N", "N", 2304, 3328, 2048) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "T", 2304, 3328, 2048) == "mfma32_128x256x32_w2x4_streamk"
     # M <= 32: the skinny, bandwidth-bound kernel.
     assert "skinny" in sel("N", "N", 16, 4096, 4096)
     assert "skinny" in sel("T", "T", 32, 128, 7)
