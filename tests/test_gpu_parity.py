@@ -239,8 +239,9 @@ def test_band_concurrent_streams():
 
 _NAMES = mg.config_names()
 STREAMK = [_NAMES.index(n) for n in ("mfma32_128x128x32_w4x2_streamk_1wg", "mfma32_128x128x32_w4x2_streamk_2wg",
-                                     "mfma32_256x128x32_w4x2_streamk", "mfma32_128x256x32_w2x4_streamk")]
-SPLIT_TILE = [i for i, n in enumerate(_NAMES) if n.startswith("mfma32_") and n.endswith("_splitk")]
+                                     "mfma32_256x128x32_w4x2_streamk", "mfma32_128x256x32_w2x4_streamk",
+                                     "mfma16_128x128x32_w4x2_streamk_1wg")]
+SPLIT_TILE = [i for i, n in enumerate(_NAMES) if n.startswith("mfma") and n.endswith("_splitk")]
 
 
 @pytest.mark.parametrize("config", STREAMK + SPLIT_TILE)
