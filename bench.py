@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "SGEMM TFLOPS (2MNK/t) at 4096^3 and % of MI355X FP32 matrix peak"
 PEAK_FP32_MATRIX_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "fp32_gemm_nn_amd", "csrc", "misgemm.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "fp32_gemm_nn_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_nn_4096.json")
 COPY_BYTES = 256 << 20
 
@@ -47,8 +47,14 @@ def tflops(flops: float, seconds: float) -> float:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over every HIP source and header of the library, by file name."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode() + b"\0")
+            with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(launch_flops_case):

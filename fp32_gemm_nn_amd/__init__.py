@@ -1,7 +1,7 @@
 """FP32 SGEMM for AMD Instinct MI355X (gfx950) -- Python binding.
 
 The work is done by the HIP library ``libmisgemm.so`` built from
-``csrc/misgemm.hip`` (see ``include/misgemm.h`` for the C ABI). This module only
+the HIP sources under ``csrc/`` (see ``include/misgemm.h`` for the C ABI). This module only
 marshals arguments into it with ctypes; it never computes a result itself and
 has no fallback: if the library is missing, every call raises.
 
