@@ -1,7 +1,7 @@
 // HBM-bound kernels for products with few rows of C (sgemm_skinny16 and the
 // split-K band kernel sgemm_skinny_band), and the small helper kernels
 // zero_ints and scale_c.
-// Internal to libmisgemm: included once, by misgemm.hip, whose header comment
+// Internal to libmisgemm: compiled only as part of misgemm.hip, whose header comment
 // describes the kernels and the configurations built from them.
 #ifndef MISGEMM_SKINNY_KERNELS_H
 #define MISGEMM_SKINNY_KERNELS_H

@@ -1,7 +1,7 @@
 // Shared pieces of the tile kernels: vector types, launch arguments, the tile
 // configuration, global -> LDS tile copies, epilogue stores, the XCD-aware tile
 // order and split bookkeeping.
-// Internal to libmisgemm: included once, by misgemm.hip, whose header comment
+// Internal to libmisgemm: compiled only as part of misgemm.hip, whose header comment
 // describes the kernels and the configurations built from them.
 #ifndef MISGEMM_TILE_COMMON_H
 #define MISGEMM_TILE_COMMON_H

@@ -1,7 +1,7 @@
 // The MFMA tile kernel sgemm_mfma32: MFMA fragments for 32 x 32 and 16 x 16
 // blocks, instruction-order hints, and the kernel with its k-loop, k-group and
 // split-K / stream-K reductions and epilogue.
-// Internal to libmisgemm: included once, by misgemm.hip, whose header comment
+// Internal to libmisgemm: compiled only as part of misgemm.hip, whose header comment
 // describes the kernels and the configurations built from them.
 #ifndef MISGEMM_TILE_KERNEL_H
 #define MISGEMM_TILE_KERNEL_H
