@@ -381,6 +381,16 @@ int select_config(char transA, char transB, int M, int N, int K) {
     if (t128 >= 144 && sk_iters >= 20LL * kNumCus) return kCfg16StreamK1;
     if (t128 >= 3 * kNumCus / 4) return cfg128;
     if (t64 >= 2 * kNumCus) return kCfg16x64;
+    // 257..511 tiles of 64 x 64 that fill 75-85% of two workgroup slots per
+    // CU, with enough k-work and B not transposed: stream-K over 128 x 128
+    // tiles keeps every CU busy for the whole k-range (NN 1280^3, beta 0.5:
+    // 48.0 vs 49.2 us for two k-groups; 1280 x 1280 x 2560: 78.6 vs 90.9).
+    // Fuller grids keep two k-groups (1408^3: 51.4 vs 55.2 us), and so do
+    // short k-work (1280 x 1280 x 640: 26.3 vs 29.9 us) and TT (1280^3, beta
+    // 0.5: 49.8 vs 53.7 us).
+    if (!op_t(transB) && t64 > kNumCus && 4 * t64 >= 3 * 2 * kNumCus && 100 * t64 < 85 * 2 * kNumCus &&
+        t128 >= 96 && sk_iters >= 3000)
+        return kCfg16StreamK1;
     // 257..511 tiles of 64 x 64: two k-groups unless their workgroups would
     // leave the CU slots badly filled; then split-K over workgroups, whose
     // smaller workgroups spread more evenly.

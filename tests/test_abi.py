@@ -131,7 +131,17 @@ def test_shape_class_selection():
     # 1024^2 output: 64 tiles of 128 x 128 only, so smaller tiles with four k-groups.
     assert sel("N", "N", 1024, 1024, 1024) == "mfma16_64x64x32_w2x2_kg4"
     assert sel("N", "N", 1000, 1300, 700) == "mfma16_64x64x32_w2x2_splitk"
-    assert sel("N", "N", 1280, 1280, 1280) == "mfma16_64x64x32_w2x2_kg2"
+    # 257..511 tiles of 64 x 64 filling 75-85% of two slots per CU, with enough
+    # k-work and B not transposed: stream-K over 128 x 128 tiles; fuller grids,
+    # short k or transposed B: two k-groups.
+    assert sel("N", "N", 1280, 1280, 1280) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("T", "N", 1280, 1280, 2560) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "N", 1536, 1024, 1024) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("T", "T", 1280, 1280, 1280) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "T", 1280, 1280, 1280) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 1280, 1280, 640) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 1408, 1408, 1408) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 1792, 1024, 1024) == "mfma16_64x64x32_w2x2_kg2"
     assert sel("N", "N", 512, 512, 512) == "mfma16_64x64x32_w2x2_splitk"
     # Up to 256 tiles of 64 x 64: split-K where the 64 x 64 timing model puts
     # it ahead of four k-groups (short grids, long K).
