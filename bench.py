@@ -370,6 +370,72 @@ def run_config_sweep(path, warmup=3):
             del prob
 
 
+def run_regret(path, shapes=90, seed=11, warmup=3):
+    """Selection check on random shapes: M and N drawn from 768..4096, K from
+    256..4096, op pairs at random (seeded). Every matrix-core tile configuration
+    is timed on each shape (best of two runs of back-to-back calls, beta = 0)
+    and select_config's pick is scored by its regret against the fastest. One
+    JSON object per shape, then a summary line."""
+    import random
+
+    import torch
+
+    import fp32_gemm_nn_amd as mg
+
+    names = mg.config_names()
+    tile_cfgs = [i for i, n in enumerate(names) if n.startswith("mfma")]
+    rng = random.Random(seed)
+    dims = [768, 1024, 1152, 1280, 1536, 1792, 2048, 2304, 2560, 3072, 3584, 4096]
+    ks = [256, 512, 1024, 2048, 4096]
+    todo = []
+    while len(todo) < shapes:
+        M, N, K = rng.choice(dims), rng.choice(dims), rng.choice(ks)
+        ops = rng.choice(["NN", "NT", "TN", "TT"])
+        if (ops, M, N, K) not in todo:
+            todo.append((ops, M, N, K))
+    torch.manual_seed(seed)
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    regrets = []
+    with open(path, "w") as out:
+        for ops, M, N, K in todo:
+            ta, tb = ops[0], ops[1]
+            A = torch.rand((K, M) if ta == "T" else (M, K), device="cuda") * 2 - 1
+            B = torch.rand((N, K) if tb == "T" else (K, N), device="cuda") * 2 - 1
+            C = torch.zeros(M, N, device="cuda")
+            chosen = mg.mi_sgemm_select_config(ta, tb, M, N, K)
+            n = max(10, min(500, int(0.04 / max(2.0 * M * N * K / 120e12, 1e-6))))
+            best = {}
+            for _ in range(2):
+                for cfg in tile_cfgs:
+                    args = (ta, tb, M, N, K, 1.0, A.data_ptr(), A.shape[1], B.data_ptr(), B.shape[1], 0.0,
+                            C.data_ptr(), N, h)
+                    for _ in range(warmup):
+                        mg.mi_sgemm_with_config(cfg, *args)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(n):
+                        rc = mg.mi_sgemm_with_config(cfg, *args)
+                    e1.record(stream)
+                    e1.synchronize()
+                    if rc != 0:
+                        raise RuntimeError(f"mi_sgemm: {mg.mi_sgemm_status_string(rc)}")
+                    best[cfg] = min(best.get(cfg, float("inf")), e0.elapsed_time(e1) * 1e3 / n)
+            fastest = min(best, key=best.get)
+            regret = best[chosen] / best[fastest] - 1
+            regrets.append(regret)
+            out.write(json.dumps({"shape": f"{ops} {M}x{N}x{K}", "chosen": names[chosen],
+                                  "chosen_us": round(best[chosen], 2), "fastest": names[fastest],
+                                  "fastest_us": round(best[fastest], 2), "regret_pct": round(100 * regret, 2),
+                                  "all_us": {names[c]: round(t, 2) for c, t in best.items()}}) + "\n")
+            out.flush()
+            del A, B, C
+        summary = {"shapes": len(regrets), "seed": seed, "mean_regret_pct": round(100 * sum(regrets) / len(regrets), 2),
+                   "above_3pct": sum(r > 0.03 for r in regrets), "max_regret_pct": round(100 * max(regrets), 2)}
+        out.write(json.dumps({"summary": summary}) + "\n")
+    print(json.dumps({"regret": summary}), file=sys.stderr)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -386,6 +452,11 @@ def main():
     ap.add_argument("--ladder", metavar="PATH",
                     help="time the vector-ALU technique ladder (valu_* configs) beside the matrix-core path at "
                          "1024^3 and 4096^3, to PATH, and exit")
+    ap.add_argument("--regret", metavar="PATH",
+                    help="time every tile configuration on random shapes and score select_config's picks by "
+                         "their regret against the fastest, to PATH, and exit")
+    ap.add_argument("--regret-shapes", type=int, default=90, help="with --regret: number of random shapes")
+    ap.add_argument("--regret-seed", type=int, default=11, help="with --regret: seed of the shape draw")
     ap.add_argument("--workload", metavar="NAME",
                     help="time only this workload (a name from synthetic/workloads.py) with its chosen "
                          "kernel and print its numbers; for profiling one configuration at a time")
@@ -414,6 +485,9 @@ def main():
         return
     if args.ladder:
         run_ladder(args.ladder)
+        return
+    if args.regret:
+        run_regret(args.regret, args.regret_shapes, args.regret_seed)
         return
 
     case = W.HEADLINE

@@ -342,6 +342,11 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // faster than as 32 x 32 blocks for every op pair (1024^3: 22 vs 24 us;
     // 2048 x 4096 x 1024 TN: 132 vs 144 us).
     const int cfg128 = kCfg16x128W42;
+    const long long kt = (K + 31) / 32;
+    // Short k (K <= 256) over at least 128 tiles of 64 x 64: the plain 64 x 64
+    // tile, whose k-loop is too short for k-groups, splits or stream-K to pay
+    // (1024 x 2048 x 256 TT: 53% of peak vs 47% two k-groups, 33% 128 x 128).
+    if (kt <= 8 && t64 >= 128) return kCfg16x64;
     if (t128 >= kNumCus) {
         const bool ta = op_t(transA), tb = op_t(transB);
         // Big tiles (one workgroup per CU) lose to 128 x 128 (two per CU)
@@ -356,16 +361,23 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const double s_q = big_ok ? (tt ? 1.065 : 1.044) * cu_balance(tiles(256, 256)) : -1.0;
         const double s_b4 = big_ok ? (tt ? 1.0 : 1.038) * cu_balance(tiles(128, 256), 2) : -1.0;
         const double s_b8 = big_ok ? (tt ? 1.034 : 1.024) * cu_balance(wide ? tiles(128, 256) : tiles(256, 128)) : -1.0;
-        const double s_128 = cu_balance(t128), s_64 = 0.87 * cu_balance(t64);
+        // The 64 x 64 tile gains on short k (K <= 512), where every larger tile
+        // spends a bigger share of its time outside the k-loop.
+        const double s_128 = cu_balance(t128), s_64 = (kt <= 16 ? 0.90 : 0.87) * cu_balance(t64);
         // Stream-K fills every CU slot whatever the tile count: with the
-        // 256 x 128 / 128 x 256 tile where big tiles pay, else 128 x 128.
-        const bool sk_ok = sk_iters >= 8LL * 2 * kNumCus;
+        // 256 x 128 / 128 x 256 tile where big tiles pay, else 128 x 128. Not
+        // below K = 1024, where its shares are too short (3584 x 2560 x 512 TT:
+        // 65% of peak vs 74% for 64 x 64).
+        const bool sk_ok = sk_iters >= 8LL * 2 * kNumCus && kt >= 32;
         const double s_skb = (sk_ok && big_ok) ? 0.955 : -1.0;
         const double s_sk = sk_ok ? 0.925 : -1.0;
         // With neither operand transposed, stream-K over 128 x 128 tiles of
         // 16 x 16 blocks, one workgroup per CU, beats the big-tile stream-K
-        // (n = 2304: 193 vs 202 us; 3840: 839 vs 854).
-        const double s_sk16 = (sk_ok && !ta && !tb) ? 0.965 : -1.0;
+        // (n = 2304: 193 vs 202 us; 3840: 839 vs 854); so it does for TN
+        // (3584 x 4096 x 1024: 82% of peak vs 76%; 2048 x 3072 x 2048: 83% vs
+        // 75%) and for TT from K = 2048 (1792 x 3584 x 2048: 80% vs 76%), while
+        // NT keeps the big-tile stream-K (1792 x 3584 x 4096: 85% vs 83%).
+        const double s_sk16 = (sk_ok && (!tb || (ta && kt >= 64))) ? 0.965 : -1.0;
         const double best =
             fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(fmax(s_128, s_64), s_sk16));
         if (best == s_q) return tt ? kCfg256x256Dl : kCfg256x256;
@@ -376,10 +388,21 @@ int select_config(char transA, char transB, int M, int N, int K) {
         if (best == s_b8) return wide ? kCfg128x256 : kCfg256x128;
         return best == s_128 ? cfg128 : kCfg16x64;
     }
-    // 144..255 tiles of 128 x 128 with at least 20 k-tiles per workgroup:
-    // stream-K, one workgroup per CU.
-    if (t128 >= 144 && sk_iters >= 20LL * kNumCus) return kCfg16StreamK1;
+    // 128..255 tiles of 128 x 128 with enough k-work per workgroup: stream-K,
+    // one workgroup per CU (1792 x 1280 x 4096 TN, 140 tiles: 78% of peak vs
+    // 58% for 64 x 64; 768 x 3072 x 1024 TN, 144 tiles: 62% vs 56%). At 128
+    // tiles it needs 20 k-tiles per workgroup (1024 x 2048 x 1024 with 16:
+    // 41.6 vs 38.8 us for 64 x 64).
+    // From about 230 tiles the data-parallel 128 x 128 tile fills the CUs well
+    // enough (3584 x 1152 x 1024 NT, 252 tiles: 79% of peak vs 69%).
+    if (t128 < 230 &&
+        ((t128 >= 144 && sk_iters >= 16LL * kNumCus) || (t128 >= 128 && sk_iters >= 20LL * kNumCus)))
+        return kCfg16StreamK1;
     if (t128 >= 3 * kNumCus / 4) return cfg128;
+    // 72..127 tiles with long k (K >= 2048): stream-K again rather than k-groups
+    // or split-K over 64 x 64 tiles (1536 x 768 x 4096 TN: 71% of peak vs 63%;
+    // 1024 x 1280 x 4096 NT: 73% vs 70%).
+    if (t128 >= 72 && kt >= 64) return kCfg16StreamK1;
     if (t64 >= 2 * kNumCus) return kCfg16x64;
     // 257..511 tiles of 64 x 64 that fill 75-85% of two workgroup slots per
     // CU, with enough k-work and B not transposed: stream-K over 128 x 128

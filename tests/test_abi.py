@@ -164,10 +164,25 @@ def test_shape_class_selection():
                     (3072, sk16), (3328, sk16), (3584, sk16), (3840, sk16), (4096, "mfma32_256x256x32_w4x2"),
                     (8192, "mfma32_256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == want, n
-    # Stream-K over big tiles for the transposed op pairs too; 128 x 128 (two
-    # per CU) where big tiles do not pay.
+    # Stream-K over big tiles for NT; over 128 x 128 tiles of 16 x 16 blocks for
+    # TN, and for TT from K = 2048; 128 x 128 (two per CU) where big tiles do not pay.
     assert sel("N", "T", 3072, 3072, 3072) == "mfma32_256x128x32_w4x2_streamk"
-    assert sel("T", "T", 2560, 2560, 2560) == "mfma32_256x128x32_w4x2_streamk"
+    assert sel("T", "N", 3072, 3072, 3072) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("T", "T", 2560, 2560, 2560) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("T", "N", 3584, 4096, 1024) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    # K <= 256 over at least 128 tiles of 64 x 64: the plain 64 x 64 tile.
+    assert sel("T", "T", 1024, 2048, 256) == "mfma16_64x64x32_w2x2"
+    assert sel("N", "N", 2560, 2560, 256) == "mfma16_64x64x32_w2x2"
+    # No stream-K below K = 1024 on big grids.
+    assert sel("T", "T", 3584, 2560, 512) == "mfma16_64x64x32_w2x2"
+    assert "streamk" not in sel("N", "T", 2304, 3072, 512)
+    # 128..229 tiles of 128 x 128 with enough k-work, or 72..127 with K >= 2048:
+    # stream-K; from 230 tiles the data-parallel 128 x 128 tile.
+    assert sel("T", "N", 1792, 1280, 4096) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("T", "N", 1536, 768, 4096) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "N", 512, 4096, 4096) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "T", 3584, 1152, 1024) == "mfma16_128x128x32_w4x2"
+    assert sel("N", "N", 1024, 2048, 1024) == "mfma16_64x64x32_w2x2"
     assert sel("N", "T", 2304, 2304, 1024) == "mfma32_128x128x32_w4x2_streamk_2wg"
     # N > M: NN takes the 16 x 16 stream-K tile; transposed B keeps the 128 x 256 stream-K tile.
     assert sel("N", "N", 2304, 3328, 2048) == "mfma16_128x128x32_w4x2_streamk_1wg"
