@@ -156,6 +156,26 @@ struct TileCopy {
         }
     }
 
+    // Complete k-tile of an edge tile, 16-byte loads only: rows at or beyond
+    // rows_left read row rows_left - 1, and chunks starting beyond the last
+    // in-range 4-aligned chunk read that chunk. The caller guarantees a 16-byte
+    // aligned base whose column offset is a multiple of 4 and ld % 4 == 0, so a
+    // clamped chunk still ends inside its row's ld floats; rows_left and
+    // cols_left are >= 1. The extra values reach only outputs beyond M or N,
+    // which are never stored.
+    __device__ __forceinline__ void load_clamped(const float *__restrict__ base, int ld, int rows_left,
+                                                 int cols_left, int tid) {
+        const int last_c = ((cols_left - 1) >> 2) << 2;
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int idx = tid + NT * j;
+            const int r = idx / CPR, c = (idx % CPR) * 4;
+            const int rr = r < rows_left ? r : rows_left - 1;
+            const int cc = c <= last_c ? c : last_c;
+            v[j] = *reinterpret_cast<const f32x4 *>(base + (size_t)rr * ld + cc);
+        }
+    }
+
     __device__ __forceinline__ void store(float *lds, int tid) const {
 #pragma unroll
         for (int j = 0; j < PER_THREAD; ++j) {

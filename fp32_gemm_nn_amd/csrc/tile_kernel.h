@@ -252,7 +252,12 @@ void sgemm_mfma32(GemmArgs g) {
         const int M = g.M, N = g.N, K = g.K;
         const bool vec = g.vec_ab != 0;
         // Interior workgroup: every complete k-tile can be fetched unguarded.
-        const bool wg_fast = (m0 + BM <= M) && (n0 + BN <= N) && vec;
+        // Edge workgroups of the register-staged tiles up to 256 x 128 take
+        // the same straight-line rounds with clamped loads (the 256 x 256 tile
+        // has no registers to spare for the clamped offsets).
+        const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
+        constexpr bool CLAMP_EDGE = !CFG::DL && BM * BN <= 256 * 128;
+        const bool wg_fast = vec && (interior || CLAMP_EDGE);
         const int kfull = K / BK;
         const int kfast_end = min(kfull, kt_end);
         const int rounds = kt_end > kt_begin ? (kt_end - kt_begin + KG - 1) / KG : 0;
@@ -267,18 +272,35 @@ void sgemm_mfma32(GemmArgs g) {
 
         ACopy ca;
         BCopy cb;
+        // A complete k-tile (kt < kfull) of a wg_fast workgroup: unguarded
+        // loads, clamped at the M and N edges (the k extent is whole). The
+        // clamps do nothing in an interior tile and are loop-invariant, so the
+        // straight-line rounds carry no branch.
         auto fetch_fast = [&](int kt) {
-            ca.load(a_ptr + kt * a_step, g.lda, 0, 0, false, true, gtid);
-            cb.load(b_ptr + kt * b_step, g.ldb, 0, 0, false, true, gtid);
+            if constexpr (CLAMP_EDGE) {
+                ca.load_clamped(a_ptr + kt * a_step, g.lda, TA ? BK : a_rows, TA ? a_cols : BK, gtid);
+                cb.load_clamped(b_ptr + kt * b_step, g.ldb, TB ? b_rows : BK, TB ? BK : b_cols, gtid);
+            } else {
+                ca.load(a_ptr + kt * a_step, g.lda, 0, 0, false, true, gtid);
+                cb.load(b_ptr + kt * b_step, g.ldb, 0, 0, false, true, gtid);
+            }
         };
         auto fetch_any = [&](int kt) {
+            if constexpr (CLAMP_EDGE) {
+                if (wg_fast && kt < kfull) {
+                    fetch_fast(kt);
+                    return;
+                }
+            }
             const int k0 = kt * BK;
-            const bool guard = !(wg_fast && kt < kfull);
-            // Rows/cols left counted from this k-tile's origin.
-            ca.load(a_ptr + kt * a_step, g.lda, TA ? a_rows - k0 : a_rows, TA ? a_cols : a_cols - k0,
-                    guard, vec, gtid);
-            cb.load(b_ptr + kt * b_step, g.ldb, TB ? b_rows : b_rows - k0, TB ? b_cols - k0 : b_cols,
-                    guard, vec, gtid);
+            // Complete k-tiles of interior workgroups unguarded (the only ones
+            // left fast without edge clamping), the rest guarded. Rows/cols
+            // left counted from this k-tile's origin.
+            const bool guard = CLAMP_EDGE || !(wg_fast && kt < kfull);
+            ca.load(a_ptr + kt * a_step, g.lda, TA ? a_rows - k0 : a_rows, TA ? a_cols : a_cols - k0, guard,
+                    vec, gtid);
+            cb.load(b_ptr + kt * b_step, g.ldb, TB ? b_rows : b_rows - k0, TB ? b_cols - k0 : b_cols, guard,
+                    vec, gtid);
         };
 
         AccT acc[FM][FN];
