@@ -31,10 +31,13 @@
 //     adjacent outputs of a row, which the epilogue stores as one vector.
 //   * LDS rows are padded by 4 floats (the padding remedy of section 3.8); the
 //     16-byte reads of the k-contiguous tiles are then bank-conflict free.
-//   * Edges: a workgroup whose tile, or whose current k-tile, crosses M, N or
-//     K takes a guarded load path that reads only in-range elements and
-//     selects zero for the rest (the zero-fill of the klklkl10086 page,
-//     01-Shared Memory Tiling); stores are masked to i < M, j < N.
+//   * Edges: a k-tile that crosses K, and a tile that crosses M or N when
+//     the operands are not 16-byte aligned with ld % 4 == 0 (or the tile is
+//     256 x 256), take a guarded load path that reads only in-range elements
+//     and selects zero for the rest (the zero-fill of the klklkl10086 page,
+//     01-Shared Memory Tiling). Other edge tiles keep the straight-line
+//     rounds with clamped loads, whose extra values only reach outputs
+//     beyond M or N. Stores are masked to i < M, j < N.
 //   * Epilogue: C = alpha*acc + beta*C fused into the store (itan.pw page,
 //     sections 3.4-3.5); when beta == 0, C is not read.
 //   * Workgroup order: consecutive workgroups are dealt round-robin to the 8
@@ -358,7 +361,11 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const bool wide = !tt && M < N;    // 128 x 256 rather than 256 x 128
         // With both transposed, the 256 x 256 tile with direct-to-LDS loads
         // (the register-staged one spills): 960 vs 989 us for 256 x 128 at 4096^3.
-        const double s_q = big_ok ? (tt ? 1.065 : 1.044) * cu_balance(tiles(256, 256)) : -1.0;
+        // Its edge tiles run the guarded k-loop (the smaller tiles clamp their
+        // edge loads instead), so a 256 x 256 grid that does not divide M and N
+        // scores lower (4000^3: 1022 us against 951 for 128 x 256 x 16).
+        const double ragged = (M % 256 != 0 || N % 256 != 0) ? 0.92 : 1.0;
+        const double s_q = big_ok ? (tt ? 1.065 : 1.044) * ragged * cu_balance(tiles(256, 256)) : -1.0;
         const double s_b4 = big_ok ? (tt ? 1.0 : 1.038) * cu_balance(tiles(128, 256), 2) : -1.0;
         const double s_b8 = big_ok ? (tt ? 1.034 : 1.024) * cu_balance(wide ? tiles(128, 256) : tiles(256, 128)) : -1.0;
         // The 64 x 64 tile gains on short k (K <= 512), where every larger tile

@@ -117,6 +117,11 @@ def test_shape_class_selection():
     assert sel("T", "T", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2_dl"
     assert sel("T", "T", 4096, 4096, 1024) == "mfma32_256x256x32_w4x2_dl"
     assert sel("T", "T", 2048, 4096, 2048) == "mfma32_256x128x32_w4x2"
+    # A 256 x 256 grid that does not divide M and N: its edge tiles run guarded,
+    # so a tile whose edges clamp their loads wins.
+    assert sel("N", "N", 4000, 4000, 4000) == "mfma32_128x256x16_w2x2"
+    assert sel("T", "T", 4000, 4000, 4000) == "mfma32_256x128x32_w4x2"
+    assert sel("N", "N", 3800, 4000, 4000) == "mfma32_128x256x16_w2x2"
     # 128 x 128 and 64 x 64 tiles run as 16 x 16 MFMA blocks, for every op pair.
     assert sel("T", "N", 2048, 2048, 2048) == "mfma16_128x128x32_w4x2"
     assert sel("T", "N", 2048, 2048, 4096) == "mfma16_128x128x32_w4x2"
