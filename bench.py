@@ -370,9 +370,10 @@ def run_config_sweep(path, warmup=3):
             del prob
 
 
-def run_regret(path, shapes=90, seed=11, warmup=3):
+def run_regret(path, shapes=90, seed=11, warmup=3, ragged=False):
     """Selection check on random shapes: M and N drawn from 768..4096, K from
-    256..4096, op pairs at random (seeded). Every matrix-core tile configuration
+    256..4096 (with ragged: M, N, K uniform over the multiples of 4 in
+    512..4096), op pairs at random (seeded). Every matrix-core tile configuration
     is timed on each shape (best of two runs of back-to-back calls, beta = 0)
     and select_config's pick is scored by its regret against the fastest. One
     JSON object per shape, then a summary line."""
@@ -389,7 +390,10 @@ def run_regret(path, shapes=90, seed=11, warmup=3):
     ks = [256, 512, 1024, 2048, 4096]
     todo = []
     while len(todo) < shapes:
-        M, N, K = rng.choice(dims), rng.choice(dims), rng.choice(ks)
+        if ragged:
+            M, N, K = (4 * rng.randint(128, 1024) for _ in range(3))
+        else:
+            M, N, K = rng.choice(dims), rng.choice(dims), rng.choice(ks)
         ops = rng.choice(["NN", "NT", "TN", "TT"])
         if (ops, M, N, K) not in todo:
             todo.append((ops, M, N, K))
@@ -430,7 +434,7 @@ def run_regret(path, shapes=90, seed=11, warmup=3):
                                   "all_us": {names[c]: round(t, 2) for c, t in best.items()}}) + "\n")
             out.flush()
             del A, B, C
-        summary = {"shapes": len(regrets), "seed": seed, "mean_regret_pct": round(100 * sum(regrets) / len(regrets), 2),
+        summary = {"shapes": len(regrets), "seed": seed, "ragged": ragged, "mean_regret_pct": round(100 * sum(regrets) / len(regrets), 2),
                    "above_3pct": sum(r > 0.03 for r in regrets), "max_regret_pct": round(100 * max(regrets), 2)}
         out.write(json.dumps({"summary": summary}) + "\n")
     print(json.dumps({"regret": summary}), file=sys.stderr)
@@ -457,6 +461,8 @@ def main():
                          "their regret against the fastest, to PATH, and exit")
     ap.add_argument("--regret-shapes", type=int, default=90, help="with --regret: number of random shapes")
     ap.add_argument("--regret-seed", type=int, default=11, help="with --regret: seed of the shape draw")
+    ap.add_argument("--regret-ragged", action="store_true",
+                    help="with --regret: draw M, N, K from the multiples of 4 in 512..4096")
     ap.add_argument("--workload", metavar="NAME",
                     help="time only this workload (a name from synthetic/workloads.py) with its chosen "
                          "kernel and print its numbers; for profiling one configuration at a time")
@@ -487,7 +493,7 @@ def main():
         run_ladder(args.ladder)
         return
     if args.regret:
-        run_regret(args.regret, args.regret_shapes, args.regret_seed)
+        run_regret(args.regret, args.regret_shapes, args.regret_seed, ragged=args.regret_ragged)
         return
 
     case = W.HEADLINE

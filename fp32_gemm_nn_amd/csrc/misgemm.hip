@@ -400,6 +400,12 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // 58% for 64 x 64; 768 x 3072 x 1024 TN, 144 tiles: 62% vs 56%). At 128
     // tiles it needs 20 k-tiles per workgroup (1024 x 2048 x 1024 with 16:
     // 41.6 vs 38.8 us for 64 x 64).
+    // Short k (K < 1024) on up to 229 tiles of 128 x 128 with at least two
+    // waves of 64 x 64 tiles: the plain 64 x 64 tile; stream-K shares are too
+    // short there and 128 x 128 spreads unevenly (1072 x 2768 x 764 NT: 43.8
+    // us against 54.3 for stream-K; 1536 x 2048 x 512: 57% of peak vs 49% for
+    // 128 x 128).
+    if (t128 < 230 && kt < 32 && t64 >= 2 * kNumCus) return kCfg16x64;
     // From about 230 tiles the data-parallel 128 x 128 tile fills the CUs well
     // enough (3584 x 1152 x 1024 NT, 252 tiles: 79% of peak vs 69%).
     if (t128 < 230 &&

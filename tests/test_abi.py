@@ -188,6 +188,9 @@ def test_shape_class_selection():
     assert sel("N", "N", 512, 4096, 4096) == "mfma16_128x128x32_w4x2_streamk_1wg"
     assert sel("N", "T", 3584, 1152, 1024) == "mfma16_128x128x32_w4x2"
     assert sel("N", "N", 1024, 2048, 1024) == "mfma16_64x64x32_w2x2"
+    # ... and short k on up to 229 such tiles: the plain 64 x 64 tile.
+    assert sel("N", "T", 1072, 2768, 764) == "mfma16_64x64x32_w2x2"
+    assert sel("N", "N", 1536, 2048, 512) == "mfma16_64x64x32_w2x2"
     assert sel("N", "T", 2304, 2304, 1024) == "mfma32_128x128x32_w4x2_streamk_2wg"
     # N > M: NN takes the 16 x 16 stream-K tile; transposed B keeps the 128 x 256 stream-K tile.
     assert sel("N", "N", 2304, 3328, 2048) == "mfma16_128x128x32_w4x2_streamk_1wg"
