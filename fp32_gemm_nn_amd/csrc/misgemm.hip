@@ -444,6 +444,14 @@ template <class CFG, bool TA, bool TB>
 hipError_t launch_t(const GemmArgs &g, unsigned workgroups, hipStream_t stream) {
     dim3 grid(workgroups);
     dim3 block(CFG::NT);
+    // Operands without 16-byte loads: the 4-byte straight-line instantiation
+    // where the tile has one, else the guarded rounds of the usual kernel.
+    if constexpr (kClampEdge<CFG>) {
+        if (!g.vec_ab) {
+            hipLaunchKernelGGL((sgemm_mfma32<CFG, TA, TB, true>), grid, block, 0, stream, g);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((sgemm_mfma32<CFG, TA, TB>), grid, block, 0, stream, g);
     return hipGetLastError();
 }

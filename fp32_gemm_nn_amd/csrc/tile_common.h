@@ -156,13 +156,15 @@ struct TileCopy {
         }
     }
 
-    // Complete k-tile of an edge tile, 16-byte loads only: rows at or beyond
-    // rows_left read row rows_left - 1, and chunks starting beyond the last
-    // in-range 4-aligned chunk read that chunk. The caller guarantees a 16-byte
-    // aligned base whose column offset is a multiple of 4 and ld % 4 == 0, so a
-    // clamped chunk still ends inside its row's ld floats; rows_left and
-    // cols_left are >= 1. The extra values reach only outputs beyond M or N,
-    // which are never stored.
+    // A complete k-tile of any tile, without branches: rows at or beyond
+    // rows_left read row rows_left - 1 (rows_left and cols_left are >= 1).
+    // VEC: 16-byte loads; a chunk starting beyond the last in-range 4-aligned
+    // chunk reads that chunk. The caller guarantees a 16-byte aligned base
+    // whose column offset is a multiple of 4 and ld % 4 == 0, so a clamped
+    // chunk still ends inside its row's ld floats. Otherwise: 4-byte loads,
+    // each column clamped to cols_left - 1, for any alignment and ld. The
+    // extra values reach only outputs beyond M or N, which are never stored.
+    template <bool VEC>
     __device__ __forceinline__ void load_clamped(const float *__restrict__ base, int ld, int rows_left,
                                                  int cols_left, int tid) {
         const int last_c = ((cols_left - 1) >> 2) << 2;
@@ -171,8 +173,16 @@ struct TileCopy {
             const int idx = tid + NT * j;
             const int r = idx / CPR, c = (idx % CPR) * 4;
             const int rr = r < rows_left ? r : rows_left - 1;
-            const int cc = c <= last_c ? c : last_c;
-            v[j] = *reinterpret_cast<const f32x4 *>(base + (size_t)rr * ld + cc);
+            if constexpr (VEC) {
+                const int cc = c <= last_c ? c : last_c;
+                v[j] = *reinterpret_cast<const f32x4 *>(base + (size_t)rr * ld + cc);
+            } else {
+                const float *p = base + (size_t)rr * ld;
+                f32x4 t;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = p[c + e < cols_left ? c + e : cols_left - 1];
+                v[j] = t;
+            }
         }
     }
 

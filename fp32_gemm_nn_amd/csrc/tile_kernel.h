@@ -201,9 +201,20 @@ __device__ __forceinline__ void schedule_iteration() {
     }
 }
 
-template <class CFG, bool TA, bool TB>
+// Register-staged tiles up to 256 x 128 fetch every complete k-tile with
+// clamped loads, so edge tiles keep the straight-line rounds (the 256 x 256
+// tile has no registers to spare for the clamped offsets).
+template <class CFG>
+constexpr bool kClampEdge = !CFG::DL && CFG::BM * CFG::BN <= 256 * 128;
+
+// SCALAR: the instantiation launched when A or B cannot be read with 16-byte
+// loads (pointer or leading dimension not a multiple of 4 floats); its
+// straight-line rounds fetch with clamped 4-byte loads. A separate kernel, so
+// that the 16-byte path keeps its own register allocation.
+template <class CFG, bool TA, bool TB, bool SCALAR = false>
 __global__ __launch_bounds__(CFG::NT) __attribute__((amdgpu_waves_per_eu(CFG::WAVES_PER_EU)))
 void sgemm_mfma32(GemmArgs g) {
+    static_assert(!SCALAR || kClampEdge<CFG>, "only clamping tiles have a 4-byte straight-line path");
     constexpr int BM = CFG::BM, BN = CFG::BN, BK = CFG::BK, NTG = CFG::NTG, KG = CFG::KG;
     constexpr int FM = CFG::FM, FN = CFG::FN, WTM = CFG::WTM, WTN = CFG::WTN;
     constexpr int Q = BK / CFG::QK;             // q-groups per k-tile
@@ -252,12 +263,11 @@ void sgemm_mfma32(GemmArgs g) {
         const int M = g.M, N = g.N, K = g.K;
         const bool vec = g.vec_ab != 0;
         // Interior workgroup: every complete k-tile can be fetched unguarded.
-        // Edge workgroups of the register-staged tiles up to 256 x 128 take
-        // the same straight-line rounds with clamped loads (the 256 x 256 tile
-        // has no registers to spare for the clamped offsets).
+        // Clamping tiles take the straight-line rounds for edge tiles too, and
+        // their SCALAR instantiation for any alignment.
         const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
-        constexpr bool CLAMP_EDGE = !CFG::DL && BM * BN <= 256 * 128;
-        const bool wg_fast = vec && (interior || CLAMP_EDGE);
+        constexpr bool CLAMP_EDGE = kClampEdge<CFG>;
+        const bool wg_fast = SCALAR || (vec && (interior || CLAMP_EDGE));
         const int kfull = K / BK;
         const int kfast_end = min(kfull, kt_end);
         const int rounds = kt_end > kt_begin ? (kt_end - kt_begin + KG - 1) / KG : 0;
@@ -278,8 +288,10 @@ void sgemm_mfma32(GemmArgs g) {
         // straight-line rounds carry no branch.
         auto fetch_fast = [&](int kt) {
             if constexpr (CLAMP_EDGE) {
-                ca.load_clamped(a_ptr + kt * a_step, g.lda, TA ? BK : a_rows, TA ? a_cols : BK, gtid);
-                cb.load_clamped(b_ptr + kt * b_step, g.ldb, TB ? b_rows : BK, TB ? BK : b_cols, gtid);
+                ca.template load_clamped<!SCALAR>(a_ptr + kt * a_step, g.lda, TA ? BK : a_rows, TA ? a_cols : BK,
+                                                  gtid);
+                cb.template load_clamped<!SCALAR>(b_ptr + kt * b_step, g.ldb, TB ? b_rows : BK, TB ? BK : b_cols,
+                                                  gtid);
             } else {
                 ca.load(a_ptr + kt * a_step, g.lda, 0, 0, false, true, gtid);
                 cb.load(b_ptr + kt * b_step, g.ldb, 0, 0, false, true, gtid);
@@ -360,8 +372,10 @@ void sgemm_mfma32(GemmArgs g) {
                 // DS reads per q-group: FM (or FN) 16-byte reads of a k-contiguous
                 // tile, four narrow reads of an m/n-contiguous one. Direct loads
                 // are issued before the round's first reads and leave no writes.
+                // A 4-byte fetch issues four loads per chunk.
                 constexpr int COPIES = CFG::DL ? 0 : ACopy::PER_THREAD + BCopy::PER_THREAD;
-                schedule_iteration<4 * FM * FN, Q, COPIES, (TA ? 4 : FM) + (TB ? FN : 4), COPIES>();
+                schedule_iteration<4 * FM * FN, Q, SCALAR ? 4 * COPIES : COPIES, (TA ? 4 : FM) + (TB ? FN : 4),
+                                   COPIES>();
                 // Direct loads complete (vmcnt) before the barrier publishes them.
                 if constexpr (CFG::DL) __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();

@@ -343,25 +343,29 @@ def _padded_ld(rows_cols, pad=4):
     return (rows_cols[1] + 3) // 4 * 4 + pad
 
 
+@pytest.mark.parametrize("layout", ["aligned", "odd_ld", "offset"])
 @pytest.mark.parametrize("config", TILE_CONFIGS)
 @pytest.mark.parametrize("ta,tb", OPS)
-def test_clamped_edge_tiles(config, ta, tb):
-    """Tiles that cross M or N with 16-byte-aligned operands and leading
-    dimensions divisible by 4 take the straight-line k-loop with clamped
-    loads: rows past M re-read the last row, column chunks past the edge
-    re-read the last aligned chunk, which may hold the NaN row padding. Only
-    outputs beyond M or N see those values; every stored output must equal the
-    oracle's bit for bit (integer inputs), with and without a k tail."""
+def test_clamped_edge_tiles(config, ta, tb, layout):
+    """Tiles that cross M or N keep the straight-line k-loop with clamped
+    loads. With 16-byte-aligned operands and leading dimensions divisible by 4
+    (aligned): rows past M re-read the last row, column chunks past the edge
+    re-read the last aligned chunk, which may hold the NaN row padding. With
+    odd leading dimensions or pointers one float off 16 bytes: the 4-byte
+    instantiation clamps every element into the matrix. Only outputs beyond M
+    or N see the extra values; every stored output must equal the oracle's bit
+    for bit (integer inputs), with and without a k tail."""
     for t, (M, N, K) in enumerate([(100, 76, 96), (5, 200, 128), (130, 3, 64), (100, 76, 100), (257, 129, 36)]):
-        case = W.Case(f"clamp_{ta}{tb}_{M}x{N}x{K}_cfg{config}", ta, tb, M, N, K, 1.0 if t % 2 else 2.0,
+        case = W.Case(f"clamp_{layout}_{ta}{tb}_{M}x{N}x{K}_cfg{config}", ta, tb, M, N, K, 1.0 if t % 2 else 2.0,
                       0.0 if t % 2 else -1.0, seed=500 + t, fill="int_rand")
         note(case.name)
         inp = W.make_inputs(case)
-        lda = _padded_ld(inp.A.shape)
-        ldb = _padded_ld(inp.B.shape)
-        ldc = _padded_ld(inp.C.shape)
+        if layout == "odd_ld":
+            lda, ldb, ldc = (_padded_ld(x.shape) + 1 for x in (inp.A, inp.B, inp.C))
+        else:
+            lda, ldb, ldc = (_padded_ld(x.shape) for x in (inp.A, inp.B, inp.C))
         want = run_oracle(case, inp)
-        got = run_gpu(case, inp, config=config, lda=lda, ldb=ldb, ldc=ldc)
+        got = run_gpu(case, inp, config=config, lda=lda, ldb=ldb, ldc=ldc, offset=1 if layout == "offset" else 0)
         compare(case, got, want, True)
 
 
