@@ -31,13 +31,14 @@
 //     adjacent outputs of a row, which the epilogue stores as one vector.
 //   * LDS rows are padded by 4 floats (the padding remedy of section 3.8); the
 //     16-byte reads of the k-contiguous tiles are then bank-conflict free.
-//   * Edges: a k-tile that crosses K, and a tile that crosses M or N when
-//     the operands are not 16-byte aligned with ld % 4 == 0 (or the tile is
-//     256 x 256), take a guarded load path that reads only in-range elements
-//     and selects zero for the rest (the zero-fill of the klklkl10086 page,
-//     01-Shared Memory Tiling). Other edge tiles keep the straight-line
-//     rounds with clamped loads, whose extra values only reach outputs
-//     beyond M or N. Stores are masked to i < M, j < N.
+//   * Edges: a k-tile that crosses K takes a guarded load path that reads
+//     only in-range elements and selects zero for the rest (the zero-fill of
+//     the klklkl10086 page, 01-Shared Memory Tiling); so do the edge tiles of
+//     the 256 x 256 tile, and all its tiles when A or B cannot be read with
+//     16-byte loads. The other tiles keep the straight-line rounds for every
+//     complete k-tile with clamped loads (16-byte, or 4-byte in a separate
+//     instantiation for unaligned operands), whose extra values only reach
+//     outputs beyond M or N. Stores are masked to i < M, j < N.
 //   * Epilogue: C = alpha*acc + beta*C fused into the store (itan.pw page,
 //     sections 3.4-3.5); when beta == 0, C is not read.
 //   * Workgroup order: consecutive workgroups are dealt round-robin to the 8
@@ -727,7 +728,15 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     g.vec_ab = aligned16(A) && aligned16(B) && lda % 4 == 0 && ldb % 4 == 0;
     g.vec_c = aligned16(C) && ldc % 4 == 0;
     const bool ta = op_t(transA), tb = op_t(transB);
-    if (config < 0) config = select_config(transA, transB, M, N, K);
+    if (config < 0) {
+        config = select_config(transA, transB, M, N, K);
+        // The 256 x 256 tile has no straight-line rounds for operands without
+        // 16-byte loads; the 256 x 128 / 128 x 256 tiles have (4096 x 4096 x
+        // 4095 NN: 1003 us on 256 x 128 against 1245; TT on 128 x 256: 1006
+        // against 1253).
+        if (!g.vec_ab && (config == kCfg256x256 || config == kCfg256x256Dl))
+            config = (ta && tb) ? kCfg128x256 : kCfg256x128;
+    }
     if ((config == kCfgSkinny16 || config == kCfgBand) && (M + 2 * 16 - 1) / (2 * 16) > 65535)
         return MISGEMM_TOO_LARGE;
     hipError_t err;

@@ -117,8 +117,10 @@ int mi_sgemm_with_config(int config, char transA, char transB, int M, int N, int
 
 /*
  * mi_sgemm_select_config: the config id mi_sgemm would use for this shape
- * (host-side decision only; no HIP call). Returns a negative status for
- * invalid trans letters or negative sizes.
+ * when A and B allow 16-byte loads (16-byte aligned pointers, lda and ldb
+ * multiples of 4); for other operands mi_sgemm replaces the 256 x 256 tiles
+ * by a 256 x 128 or 128 x 256 one. Host-side decision only; no HIP call.
+ * Returns a negative status for invalid trans letters or negative sizes.
  */
 int mi_sgemm_select_config(char transA, char transB, int M, int N, int K);
 

@@ -369,6 +369,24 @@ def test_clamped_edge_tiles(config, ta, tb, layout):
         compare(case, got, want, True)
 
 
+@pytest.mark.parametrize("ta,tb,M,N,K,layout", [("N", "N", 4096, 4096, 2048, "offset"),
+                                                 ("T", "T", 4096, 4096, 1024, "odd_ld")])
+def test_unaligned_operands_on_256x256_shapes(ta, tb, M, N, K, layout):
+    """Shapes whose pick for 16-byte-loadable operands is a 256 x 256 tile:
+    with unaligned operands mi_sgemm runs a 256 x 128 or 128 x 256 tile
+    instead (4-byte straight-line rounds). Bit-exact on integer inputs."""
+    assert "256x256" in mg.config_names()[mg.mi_sgemm_select_config(ta, tb, M, N, K)]
+    case = W.Case(f"unaligned_{layout}_{ta}{tb}_{M}x{N}x{K}", ta, tb, M, N, K, 1.0, -1.0, seed=61, fill="int_rand")
+    note(case.name)
+    inp = W.make_inputs(case)
+    if layout == "odd_ld":
+        lda, ldb, ldc = (x.shape[1] + 1 for x in (inp.A, inp.B, inp.C))
+        got = run_gpu(case, inp, lda=lda, ldb=ldb, ldc=ldc)
+    else:
+        got = run_gpu(case, inp, offset=1)
+    compare(case, got, run_oracle(case, inp), True)
+
+
 @pytest.mark.parametrize("config", range(NCONFIG))
 @pytest.mark.parametrize("ta,tb", OPS)
 def test_every_config_uniform_medium(config, ta, tb):
