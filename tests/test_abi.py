@@ -106,6 +106,28 @@ def test_with_config_rejects_unknown_id():
     assert mg.mi_sgemm_with_config(n, *args, 0) == -3
 
 
+def test_selection_fuzz():
+    """Seeded random shapes: the pick is always a valid matrix-core
+    configuration (never a vector-ALU ladder rung), the band kernel exactly
+    when M <= 32 and N >= 128, and the direct-to-LDS 256 x 256 tile only for TT."""
+    import random
+
+    names = mg.config_names()
+    rng = random.Random(5)
+    for _ in range(5000):
+        M = rng.choice([rng.randint(1, 64), rng.randint(1, 5000), rng.randint(1, 20000)])
+        N = rng.choice([rng.randint(1, 256), rng.randint(1, 5000), rng.randint(1, 20000)])
+        K = rng.choice([rng.randint(0, 64), rng.randint(1, 5000), rng.randint(1, 20000)])
+        ta, tb = rng.choice("NnTtCc"), rng.choice("NnTtCc")
+        c = mg.mi_sgemm_select_config(ta, tb, M, N, K)
+        assert 0 <= c < len(names), (ta, tb, M, N, K, c)
+        name = names[c]
+        assert not name.startswith("valu_"), (ta, tb, M, N, K, name)
+        assert ("band" in name) == (M <= 32 and N >= 128), (ta, tb, M, N, K, name)
+        if name.endswith("_dl"):
+            assert ta in "TtCc" and tb in "TtCc" and name == "mfma32_256x256x32_w4x2_dl", (ta, tb, M, N, K, name)
+
+
 def test_shape_class_selection():
     names = mg.config_names()
     sel = lambda *s: names[mg.mi_sgemm_select_config(*s)]
