@@ -407,6 +407,10 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // us against 54.3 for stream-K; 1536 x 2048 x 512: 57% of peak vs 49% for
     // 128 x 128).
     if (t128 < 230 && kt < 32 && t64 >= 2 * kNumCus) return kCfg16x64;
+    // 461..511 tiles of 64 x 64 fill two k-group workgroups per CU to 90% or
+    // more, which beats stream-K (1844 x 1056 x 2032 NN: 73.3 us against 81.6;
+    // 828 x 2392 x 3588 NT: 7.9% faster).
+    if (t128 < 230 && 10 * t64 >= 9 * 2 * kNumCus && t64 < 2 * kNumCus) return kCfg16x64Kg2;
     // From about 230 tiles the data-parallel 128 x 128 tile fills the CUs well
     // enough (3584 x 1152 x 1024 NT, 252 tiles: 79% of peak vs 69%).
     if (t128 < 230 &&

@@ -210,6 +210,10 @@ def test_shape_class_selection():
     assert sel("N", "N", 512, 4096, 4096) == "mfma16_128x128x32_w4x2_streamk_1wg"
     assert sel("N", "T", 3584, 1152, 1024) == "mfma16_128x128x32_w4x2"
     assert sel("N", "N", 1024, 2048, 1024) == "mfma16_64x64x32_w2x2"
+    # ... and 461..511 tiles of 64 x 64 (two k-group workgroups fill 90% of the
+    # slots): two k-groups; exactly 512 keeps stream-K.
+    assert sel("N", "N", 1844, 1056, 2032) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "T", 828, 2392, 3588) == "mfma16_64x64x32_w2x2_kg2"
     # ... and short k on up to 229 such tiles: the plain 64 x 64 tile.
     assert sel("N", "T", 1072, 2768, 764) == "mfma16_64x64x32_w2x2"
     assert sel("N", "N", 1536, 2048, 512) == "mfma16_64x64x32_w2x2"
