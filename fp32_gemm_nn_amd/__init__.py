@@ -118,12 +118,27 @@ def config_names() -> list[str]:
 
 
 def _ld(t) -> int:
-    """Row stride of a 2-D tensor whose rows are contiguous (stride(1) == 1)."""
+    """Leading dimension of a 2-D tensor whose rows are contiguous (stride(1) == 1).
+
+    With more than one row it is the row stride, which must be at least the
+    row length: a smaller one (rows that overlap, or stride 0 from expand())
+    cannot be described by a leading dimension, and passing the row length
+    instead would make the kernels address elements the tensor does not hold.
+    Such tensors raise ValueError before anything is launched. A single row
+    has no row stride to honour, so its row length (at least 1) is passed.
+    """
     if t.dim() != 2:
         raise ValueError("expected a 2-D tensor")
-    if t.shape[1] > 1 and t.stride(1) != 1:
+    rows, cols = int(t.shape[0]), int(t.shape[1])
+    if cols > 1 and t.stride(1) != 1:
         raise ValueError("rows must be contiguous (stride(1) == 1); pass op 'T' for transposes")
-    return max(int(t.stride(0)), int(t.shape[1]), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
+    if rows <= 1:
+        return max(cols, 1)
+    ld = int(t.stride(0))
+    if ld < max(cols, 1):
+        raise ValueError(f"row stride {ld} is smaller than the row length {cols} (overlapping or broadcast "
+                         "rows have no leading dimension); pass a tensor with distinct rows, e.g. .contiguous()")
+    return ld
 
 
 def _overlaps(x, y) -> bool:
@@ -131,7 +146,8 @@ def _overlaps(x, y) -> bool:
     (C must not overlap A or B). Row i of x covers bytes [x0 + i*sx, x0 + i*sx + wx);
     for each row of x the rows of y that could intersect it form one index
     range, so the test is exact (padding between rows is not counted) and
-    linear in the rows of x."""
+    linear in the rows of x. The row strides are the leading dimensions of
+    _ld, so a tensor with overlapping or broadcast rows raises ValueError."""
     import numpy as np
 
     if x.numel() == 0 or y.numel() == 0:
@@ -139,7 +155,7 @@ def _overlaps(x, y) -> bool:
     es = x.element_size()
 
     def rows(t):
-        return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else 1) * es, t.shape[1] * es, t.shape[0]
+        return t.data_ptr(), _ld(t) * es, t.shape[1] * es, t.shape[0]
 
     x0, sx, wx, rx = rows(x)
     y0, sy, wy, ry = rows(y)
@@ -169,6 +185,7 @@ def sgemm(transA: str, transB: str, alpha: float, A, B, beta: float, C, stream=N
             raise ValueError(f"{name} must be a device tensor")
     if not (A.device == B.device == C.device):
         raise ValueError(f"A, B and C must be on one device (got {A.device}, {B.device}, {C.device})")
+    lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
     if _overlaps(C, A) or _overlaps(C, B):
         raise ValueError("C must not overlap A or B")
     ta = transA in ("T", "t", "C", "c")
@@ -182,8 +199,8 @@ def sgemm(transA: str, transB: str, alpha: float, A, B, beta: float, C, stream=N
         raise ValueError(f"shape mismatch: op(A) {am}x{K}, op(B) {bk}x{bn}, C {M}x{N}")
     if stream is None:
         stream = torch.cuda.current_stream(C.device).cuda_stream
-    args = (transA, transB, M, N, K, alpha, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), beta,
-            C.data_ptr(), _ld(C), stream)
+    args = (transA, transB, M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb, beta,
+            C.data_ptr(), ldc, stream)
     rc = mi_sgemm(*args) if config is None else mi_sgemm_with_config(config, *args)
     if rc != 0:
         raise MisgemmError(rc)

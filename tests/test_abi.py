@@ -287,3 +287,48 @@ def test_wrapper_overlap_check():
         views.append(buf[off:off + r * ld].view(r, ld)[:, :c])
     for x, y in itertools.combinations(views, 2):
         assert mg._overlaps(x, y) == bool(addrs(x) & addrs(y))
+
+
+def test_wrapper_leading_dimension():
+    """The tensor wrapper's leading dimension: the row stride for tensors with
+    distinct rows, the row length for a single row, and ValueError (before any
+    launch) for rows that overlap or are broadcast, whose elements no leading
+    dimension can address."""
+    torch = pytest.importorskip("torch")
+
+    buf = torch.zeros(100)
+    assert mg._ld(buf[:12].view(3, 4)) == 4                       # packed
+    assert mg._ld(buf[:60].view(6, 10)[:, :7]) == 10              # padded rows
+    assert mg._ld(buf[:4].view(1, 4)) == 4                        # one row
+    assert mg._ld(buf[:1].view(1, 1)) == 1
+    assert mg._ld(buf[10:13].view(1, 3)) == 3
+    assert mg._ld(buf[:5].view(5, 1)) == 1                        # one column, stride 1
+    assert mg._ld(torch.zeros(3, 0)) >= 1
+    assert mg._ld(torch.zeros(4).expand(1, 4)) == 4                # one broadcast row is still one row
+    with pytest.raises(ValueError, match="row stride"):
+        mg._ld(torch.zeros(4).expand(3, 4))                       # stride (0, 1): 4 floats of storage
+    with pytest.raises(ValueError, match="row stride"):
+        mg._ld(buf.as_strided((3, 4), (2, 1)))                    # overlapping rows
+    with pytest.raises(ValueError, match="row stride"):
+        mg._ld(torch.zeros(1).expand(3, 1))                       # stride 0, one column
+    with pytest.raises(ValueError, match="contiguous"):
+        mg._ld(buf[:12].view(3, 4).t())                           # transposed view: pass op 'T'
+    with pytest.raises(ValueError):
+        mg._ld(buf[:8])                                           # not 2-D
+    # The overlap check rejects the same tensors instead of dividing by a zero stride.
+    with pytest.raises(ValueError, match="row stride"):
+        mg._overlaps(torch.zeros(4).expand(3, 4), buf[:12].view(3, 4))
+    with pytest.raises(ValueError, match="row stride"):
+        mg._overlaps(buf[:12].view(3, 4), buf.as_strided((3, 4), (2, 1)))
+
+
+def test_wrapper_rejects_broadcast_before_launch():
+    """sgemm() on CPU tensors with a broadcast C fails on the device check or
+    on the leading dimension, never reaching the library."""
+    torch = pytest.importorskip("torch")
+
+    A = torch.zeros(3, 4)
+    B = torch.zeros(4, 4)
+    C = torch.zeros(4).expand(3, 4)
+    with pytest.raises(ValueError):
+        mg.sgemm("N", "N", 1.0, A, B, 0.0, C)
