@@ -470,6 +470,9 @@ constexpr int kWsCounters = 1 << 16;
 struct Workspace {
     float *partials = nullptr;
     int *counters = nullptr;
+    // Handed out while the stream was being captured into a graph: the graph
+    // holds its address, so it is never freed.
+    bool pinned = false;
 };
 
 std::mutex g_ws_mutex;
@@ -499,19 +502,32 @@ struct DeviceGuard {
     }
 };
 
+// Whether work enqueued on `stream` now would be captured into a graph (an
+// unknown status counts as capturing).
+bool capturing(hipStream_t stream) {
+    if (stream == nullptr) return false;
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &capture) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return capture != hipStreamCaptureStatusNone;
+}
+
 const Workspace *get_workspace(hipStream_t stream) {
     int dev = 0;
     if (!stream_device(stream, dev)) return nullptr;
+    const bool in_capture = capturing(stream);
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     auto key = std::make_pair(dev, stream);
     auto it = g_ws.find(key);
-    if (it != g_ws.end()) return &it->second;
+    if (it != g_ws.end()) {
+        if (in_capture) it->second.pinned = true;
+        return &it->second;
+    }
     // No allocation while the stream is being captured into a graph: the
     // captured call runs unsplit instead.
-    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-    if (stream != nullptr &&
-        (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone))
-        return nullptr;
+    if (in_capture) return nullptr;
     DeviceGuard on_dev(dev);
     if (!on_dev.ok) return nullptr;
     Workspace w;
@@ -831,6 +847,8 @@ extern "C" int mi_sgemm_release_workspace(hipStream_t stream) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     auto it = g_ws.find(std::make_pair(dev, stream));
     if (it == g_ws.end()) return MISGEMM_SUCCESS;
+    // A captured graph's kernels hold this workspace's address: keep it.
+    if (it->second.pinned) return MISGEMM_WORKSPACE_CAPTURED;
     DeviceGuard on_dev(dev);
     if (!on_dev.ok) return MISGEMM_LAUNCH_FAILED;
     if (hipStreamSynchronize(stream) != hipSuccess) return MISGEMM_LAUNCH_FAILED;
@@ -864,6 +882,7 @@ extern "C" const char *mi_sgemm_status_string(int status) {
         case MISGEMM_BAD_CONFIG: return "unknown kernel configuration id";
         case MISGEMM_TOO_LARGE: return "problem too large (leading dimension beyond 32-bit tile offsets, or grid too large)";
         case MISGEMM_LAUNCH_FAILED: return "HIP kernel launch failed";
+        case MISGEMM_WORKSPACE_CAPTURED: return "workspace is used by a captured HIP graph and stays allocated until the process ends";
         default: return "unknown status";
     }
 }

@@ -29,8 +29,14 @@
 extern "C" {
 #endif
 
-/* Status codes. Negative values name the offending argument by its position
- * in mi_sgemm's parameter list (BLAS "info" convention). */
+/* Status codes. Every entry point returns one, so that no failure passes
+ * silently: the youngju.dev CUDA architecture primer (section
+ * よくある落とし穴とチェックリスト, item 6, エラーチェックの省略) warns that
+ * unchecked runtime return codes and launch errors yield wrong results
+ * without a sign, and advises checking each call and the last launch error.
+ * Negative values name the offending argument by its position in mi_sgemm's
+ * parameter list (BLAS "info" convention) and are returned before any HIP
+ * call; positive values report the HIP runtime. */
 #define MISGEMM_SUCCESS          0
 #define MISGEMM_BAD_TRANSA      (-1)
 #define MISGEMM_BAD_TRANSB      (-2)
@@ -46,6 +52,7 @@ extern "C" {
 #define MISGEMM_BAD_CONFIG      (-20)
 #define MISGEMM_TOO_LARGE       (-21)
 #define MISGEMM_LAUNCH_FAILED     1
+#define MISGEMM_WORKSPACE_CAPTURED 2
 
 /*
  * mi_sgemm: C <- alpha * op(A) * op(B) + beta * C   (FP32, row-major)
@@ -84,8 +91,9 @@ extern "C" {
  * enqueues kernels only (no memset); split-K and stream-K kernels reset
  * their own counters. Make one eager call that splits on the capture stream
  * first, so that its workspace exists before capture (otherwise the captured
- * call runs unsplit). Replays use that stream's workspace: do not run them
- * concurrently with other calls on that stream.
+ * call runs unsplit). Replays use that stream's workspace: they must not
+ * overlap one another or other calls on that stream, and the workspace is
+ * then kept until the process ends (see mi_sgemm_release_workspace).
  *
  * Alignment: any pointer and leading dimension is accepted. 16-byte aligned
  * pointers with lda, ldb, ldc multiples of 4 take the dwordx4 path.
@@ -129,7 +137,10 @@ int mi_sgemm_select_config(char transA, char transB, int M, int N, int K);
 int mi_sgemm_config_count(void);
 const char *mi_sgemm_config_name(int config);
 
-/* Static description of a status code (never NULL; owned by the library). */
+/* Static description of a status code (never NULL; owned by the library),
+ * so that a caller can report each checked return code in words (the
+ * youngju.dev CUDA architecture primer, section よくある落とし穴とチェックリスト,
+ * item 6, エラーチェックの省略). */
 const char *mi_sgemm_status_string(int status);
 
 /*
@@ -139,8 +150,12 @@ const char *mi_sgemm_status_string(int status);
  * which ran split products: call it before hipStreamDestroy to return the
  * memory. A later split call on the stream allocates a fresh workspace.
  * Returns MISGEMM_SUCCESS (also when there was none), or
- * MISGEMM_LAUNCH_FAILED if waiting for the stream or freeing failed. It must
- * not run while another thread enqueues an mi_sgemm call on the same stream.
+ * MISGEMM_LAUNCH_FAILED if waiting for the stream or freeing failed. A
+ * workspace that a call captured into a HIP graph uses is never freed (the
+ * graph's kernels hold its address): release then returns
+ * MISGEMM_WORKSPACE_CAPTURED and the workspace stays until the process ends.
+ * It must not run while another thread enqueues an mi_sgemm call on the same
+ * stream.
  */
 int mi_sgemm_release_workspace(hipStream_t stream);
 

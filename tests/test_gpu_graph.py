@@ -69,6 +69,18 @@ def test_graph_replays_match_eager(case):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(C, want[k]), f"replay {rep} differs from the eager result"
+    # The captured kernels hold the stream's workspace: releasing it is
+    # refused while it is pinned, and the graph still replays correctly.
+    name = mg.config_names()[mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)]
+    uses_ws = "split" in name or "streamk" in name
+    assert mg.mi_sgemm_release_workspace(h) == (2 if uses_ws else 0), name
+    C.copy_(C_in)
+    A.copy_(A0)
+    B.copy_(B0)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(C, want[0]), "replay after the refused release differs"
     del graph
 
 
