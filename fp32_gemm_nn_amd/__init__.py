@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "MisgemmError", "library_path", "load_library",
-    "mi_sgemm", "mi_sgemm_with_config", "mi_sgemm_select_config",
+    "mi_sgemm", "mi_sgemm_noalloc", "mi_sgemm_with_config", "mi_sgemm_select_config",
     "mi_sgemm_config_count", "mi_sgemm_config_name", "mi_sgemm_status_string",
     "mi_sgemm_release_workspace", "sgemm", "config_names",
 ]
@@ -52,6 +52,8 @@ def load_library():
     gemm_args = [c, c, i, i, i, f, p, i, p, i, f, p, i, p]
     lib.mi_sgemm.argtypes = gemm_args
     lib.mi_sgemm.restype = i
+    lib.mi_sgemm_noalloc.argtypes = gemm_args
+    lib.mi_sgemm_noalloc.restype = i
     lib.mi_sgemm_with_config.argtypes = [i, *gemm_args]
     lib.mi_sgemm_with_config.restype = i
     lib.mi_sgemm_select_config.argtypes = [c, c, i, i, i]
@@ -82,6 +84,13 @@ def mi_sgemm(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, strea
     return load_library().mi_sgemm(_ch(transA), _ch(transB), int(M), int(N), int(K), float(alpha),
                                    A or None, int(lda), B or None, int(ldb), float(beta), C or None,
                                    int(ldc), stream or None)
+
+
+def mi_sgemm_noalloc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    """C ABI mi_sgemm_noalloc (no device allocation; the device's static scratch)."""
+    return load_library().mi_sgemm_noalloc(_ch(transA), _ch(transB), int(M), int(N), int(K), float(alpha),
+                                           A or None, int(lda), B or None, int(ldb), float(beta), C or None,
+                                           int(ldc), stream or None)
 
 
 def mi_sgemm_with_config(config, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,

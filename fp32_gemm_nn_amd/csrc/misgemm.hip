@@ -63,7 +63,8 @@
 //
 // Files: tile_common.h (tile configuration, global -> LDS copies, stores,
 // tile order, split bookkeeping), tile_kernel.h (MFMA fragments and the tile
-// kernel), skinny_kernels.h (few-row kernels, helpers); this file holds the
+// kernel), skinny_kernels.h (few-row kernels, helpers), scratch.hip (the
+// static device scratch of mi_sgemm_noalloc); this file holds the
 // configuration table, shape-class selection, workspace, launch and C ABI.
 
 #include <hip/hip_runtime.h>
@@ -78,6 +79,7 @@
 
 #include "misgemm.h"
 #include "ladder.h"
+#include "scratch.h"
 #include "skinny_kernels.h"
 #include "tile_common.h"
 #include "tile_kernel.h"
@@ -463,9 +465,13 @@ hipError_t launch_t(const GemmArgs &g, unsigned workgroups, hipStream_t stream) 
 
 // Workspace for the split-K reduction, one per (device, stream) so that calls
 // on different streams never share partials or counters. Allocated on the
-// first call that needs it and kept until the process ends.
+// first call that needs it and kept until mi_sgemm_release_workspace or the
+// end of the process. mi_sgemm_noalloc uses the device's static scratch of the
+// same capacity instead, so both make the same split plans.
 constexpr size_t kWsFloats = size_t(16) << 20;  // 64 MiB of partial blocks
 constexpr int kWsCounters = 1 << 16;
+static_assert(kWsFloats == misgemm_scratch::kPartialFloats && kWsCounters == misgemm_scratch::kCounters,
+              "the static scratch has a stream workspace's capacity");
 
 struct Workspace {
     float *partials = nullptr;
@@ -549,6 +555,24 @@ const Workspace *get_workspace(hipStream_t stream) {
     return &g_ws.emplace(key, w).first->second;
 }
 
+// Where a call's split-K exchange space comes from: the stream's workspace
+// (mi_sgemm, allocated on first use) or a fixed one (mi_sgemm_noalloc: the
+// device's static scratch, never allocated). With a fixed one, a plan whose
+// partial blocks or counters would not fit is refused: `overflow` is set and
+// the launcher enqueues nothing.
+struct WsSource {
+    const Workspace *fixed = nullptr;
+    bool overflow = false;
+    const Workspace *get(hipStream_t stream, size_t floats, long long counters) {
+        if (fixed == nullptr) return get_workspace(stream);
+        if (floats > kWsFloats || counters > (long long)kWsCounters) {
+            overflow = true;
+            return nullptr;
+        }
+        return fixed;
+    }
+};
+
 // Split factor for the band kernel: enough workgroups to fill every CU's
 // workgroup slots once (the LDS partial blocks limit how many fit on a CU),
 // at least one 16-row chunk per wave, within the workspace.
@@ -586,7 +610,7 @@ hipError_t launch_band_mb(bool ta, bool tb, const SplitArgs &sa, hipStream_t str
     return launch_band_t<MB, true, true, FAST>(sa, stream);
 }
 
-hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) {
+hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream, WsSource &wsrc) {
     const int mb = g.M <= 16 ? 1 : 2;
     SplitArgs sa;
     sa.g = g;
@@ -596,7 +620,9 @@ hipError_t launch_band(bool ta, bool tb, const GemmArgs &g, hipStream_t stream) 
     const bool fast = g.vec_ab && g.N % kBandCols == 0 && g.K % 16 == 0;
     int S = band_splits(g.M, g.N, g.K, mb, fast);
     if (S > 1) {
-        const Workspace *w = get_workspace(stream);
+        const long long tiles = (long long)((g.N + kBandCols - 1) / kBandCols) * ((g.M + 16 * mb - 1) / (16 * mb));
+        const Workspace *w = wsrc.get(stream, (size_t)tiles * S * 16 * mb * kBandCols, tiles);
+        if (wsrc.overflow) return hipSuccess;
         if (w == nullptr) {
             S = 1;
         } else {
@@ -634,7 +660,7 @@ hipError_t launch_skinny(bool ta, bool tb, const GemmArgs &g, hipStream_t stream
 }
 
 template <class CFG>
-hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int split_slots = 0) {
+hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, WsSource &wsrc, int split_slots = 0) {
     g.tiles_m = (g.M + CFG::BM - 1) / CFG::BM;
     g.tiles_n = (g.N + CFG::BN - 1) / CFG::BN;
     const int ktiles = (g.K + CFG::BK - 1) / CFG::BK;
@@ -660,7 +686,8 @@ hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int spl
         while (S > 1 && tiles * S * CFG::BM * CFG::BN > (long long)kWsFloats) --S;
         if (tiles > kWsCounters) S = 1;
         if (S > 1) {
-            const Workspace *w = get_workspace(stream);
+            const Workspace *w = wsrc.get(stream, (size_t)tiles * S * CFG::BM * CFG::BN, tiles);
+            if (wsrc.overflow) return hipSuccess;
             if (w == nullptr) {
                 S = 1;
             } else {
@@ -685,7 +712,10 @@ hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int spl
         long long G = std::min(tiles * ktiles, (long long)kNumCus * per_cu);
         G = std::min(G, (long long)(kWsFloats / ((size_t)2 * CFG::BM * CFG::BN)));
         if (tiles % G != 0) {
-            const Workspace *w = tiles <= kWsCounters ? get_workspace(stream) : nullptr;
+            // Partial slots 0 .. 2G-1 and one counter per tile.
+            const Workspace *w =
+                tiles <= kWsCounters ? wsrc.get(stream, (size_t)2 * G * CFG::BM * CFG::BN, tiles) : nullptr;
+            if (wsrc.overflow) return hipSuccess;
             if (w == nullptr) {
                 G = tiles;
             } else {
@@ -709,7 +739,7 @@ hipError_t launch_cfg(bool ta, bool tb, GemmArgs &g, hipStream_t stream, int spl
 }
 
 int run(int config, char transA, char transB, int M, int N, int K, float alpha, const float *A, int lda,
-        const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+        const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream, bool noalloc = false) {
     int rc = check_args(transA, transB, M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != MISGEMM_SUCCESS) return rc;
     if (config < -1 || config >= kNumConfigs) return MISGEMM_BAD_CONFIG;
@@ -759,6 +789,25 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     }
     if ((config == kCfgSkinny16 || config == kCfgBand) && (M + 2 * 16 - 1) / (2 * 16) > 65535)
         return MISGEMM_TOO_LARGE;
+    WsSource wsrc;
+    Workspace fixed;
+    if (noalloc) {
+        // The device's static scratch; on the first call for a device, clear
+        // its counters on this stream unless the stream is being captured
+        // (the array starts zero-filled, and every split product leaves its
+        // counters at zero).
+        int dev = 0;
+        bool first = false;
+        if (!stream_device(stream, dev) ||
+            !misgemm_scratch::device_scratch(dev, &fixed.partials, &fixed.counters, &first))
+            return MISGEMM_LAUNCH_FAILED;
+        if (first && !capturing(stream)) {
+            hipLaunchKernelGGL(zero_ints, dim3((kWsCounters + 255) / 256), dim3(256), 0, stream, fixed.counters,
+                               kWsCounters);
+            if (hipGetLastError() != hipSuccess) return MISGEMM_LAUNCH_FAILED;
+        }
+        wsrc.fixed = &fixed;
+    }
     hipError_t err;
     if (config >= kCfgLadderFirst && config <= kCfgLadderLast) {
         misgemm_ladder::LadderArgs la;
@@ -779,39 +828,40 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
     }
     switch (config) {
-        case kCfg128: err = launch_cfg<CfgL>(ta, tb, g, stream); break;
-        case kCfg64: err = launch_cfg<CfgS>(ta, tb, g, stream); break;
+        case kCfg128: err = launch_cfg<CfgL>(ta, tb, g, stream, wsrc); break;
+        case kCfg64: err = launch_cfg<CfgS>(ta, tb, g, stream, wsrc); break;
         case kCfgSkinny16: err = launch_skinny(ta, tb, g, stream); break;
-        case kCfgBand: err = launch_band(ta, tb, g, stream); break;
-        case kCfg64Kg2: err = launch_cfg<CfgS2>(ta, tb, g, stream); break;
-        case kCfg64Kg4: err = launch_cfg<CfgS4>(ta, tb, g, stream); break;
-        case kCfg128Kg2: err = launch_cfg<CfgL2>(ta, tb, g, stream); break;
-        case kCfg128W24: err = launch_cfg<CfgL24>(ta, tb, g, stream); break;
-        case kCfg128W42: err = launch_cfg<CfgL42>(ta, tb, g, stream); break;
-        case kCfg256x128: err = launch_cfg<CfgW>(ta, tb, g, stream); break;
-        case kCfg128x256: err = launch_cfg<CfgT>(ta, tb, g, stream); break;
-        case kCfg128W42Split: err = launch_cfg<CfgL42K>(ta, tb, g, stream, 1); break;
-        case kCfg64Split: err = launch_cfg<CfgSK>(ta, tb, g, stream, 2); break;
-        case kCfg128Split: err = launch_cfg<CfgLK>(ta, tb, g, stream, 1); break;
-        case kCfg128x256x16: err = launch_cfg<CfgT16>(ta, tb, g, stream); break;
-        case kCfg256x256: err = launch_cfg<CfgQ32>(ta, tb, g, stream); break;
-        case kCfgStreamK1: err = launch_cfg<CfgL42S1>(ta, tb, g, stream); break;
-        case kCfgStreamK2: err = launch_cfg<CfgL42S2>(ta, tb, g, stream); break;
-        case kCfgStreamK256x128: err = launch_cfg<CfgWS>(ta, tb, g, stream); break;
-        case kCfg256x256Dl: err = launch_cfg<CfgQ32D>(ta, tb, g, stream); break;
-        case kCfg128W42Dl: err = launch_cfg<CfgL42D>(ta, tb, g, stream); break;
-        case kCfg16x64: err = launch_cfg<Cfg16S>(ta, tb, g, stream); break;
-        case kCfg16x64Kg2: err = launch_cfg<Cfg16S2>(ta, tb, g, stream); break;
-        case kCfg16x64Kg4: err = launch_cfg<Cfg16S4>(ta, tb, g, stream); break;
-        case kCfg16x64Split: err = launch_cfg<Cfg16SK>(ta, tb, g, stream, 2); break;
-        case kCfg16x128W42: err = launch_cfg<Cfg16L42>(ta, tb, g, stream); break;
-        case kCfg16StreamK1: err = launch_cfg<Cfg16L42S1>(ta, tb, g, stream); break;
-        case kCfg16x128: err = launch_cfg<Cfg16L>(ta, tb, g, stream); break;
-        case kCfg16x256x128: err = launch_cfg<Cfg16W>(ta, tb, g, stream); break;
-        case kCfg16x128W42Dl: err = launch_cfg<Cfg16L42D>(ta, tb, g, stream); break;
-        case kCfg16x64Kg4Dl: err = launch_cfg<Cfg16S4D>(ta, tb, g, stream); break;
-        default: err = launch_cfg<CfgTS>(ta, tb, g, stream); break;   // kCfgStreamK128x256
+        case kCfgBand: err = launch_band(ta, tb, g, stream, wsrc); break;
+        case kCfg64Kg2: err = launch_cfg<CfgS2>(ta, tb, g, stream, wsrc); break;
+        case kCfg64Kg4: err = launch_cfg<CfgS4>(ta, tb, g, stream, wsrc); break;
+        case kCfg128Kg2: err = launch_cfg<CfgL2>(ta, tb, g, stream, wsrc); break;
+        case kCfg128W24: err = launch_cfg<CfgL24>(ta, tb, g, stream, wsrc); break;
+        case kCfg128W42: err = launch_cfg<CfgL42>(ta, tb, g, stream, wsrc); break;
+        case kCfg256x128: err = launch_cfg<CfgW>(ta, tb, g, stream, wsrc); break;
+        case kCfg128x256: err = launch_cfg<CfgT>(ta, tb, g, stream, wsrc); break;
+        case kCfg128W42Split: err = launch_cfg<CfgL42K>(ta, tb, g, stream, wsrc, 1); break;
+        case kCfg64Split: err = launch_cfg<CfgSK>(ta, tb, g, stream, wsrc, 2); break;
+        case kCfg128Split: err = launch_cfg<CfgLK>(ta, tb, g, stream, wsrc, 1); break;
+        case kCfg128x256x16: err = launch_cfg<CfgT16>(ta, tb, g, stream, wsrc); break;
+        case kCfg256x256: err = launch_cfg<CfgQ32>(ta, tb, g, stream, wsrc); break;
+        case kCfgStreamK1: err = launch_cfg<CfgL42S1>(ta, tb, g, stream, wsrc); break;
+        case kCfgStreamK2: err = launch_cfg<CfgL42S2>(ta, tb, g, stream, wsrc); break;
+        case kCfgStreamK256x128: err = launch_cfg<CfgWS>(ta, tb, g, stream, wsrc); break;
+        case kCfg256x256Dl: err = launch_cfg<CfgQ32D>(ta, tb, g, stream, wsrc); break;
+        case kCfg128W42Dl: err = launch_cfg<CfgL42D>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x64: err = launch_cfg<Cfg16S>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x64Kg2: err = launch_cfg<Cfg16S2>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x64Kg4: err = launch_cfg<Cfg16S4>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x64Split: err = launch_cfg<Cfg16SK>(ta, tb, g, stream, wsrc, 2); break;
+        case kCfg16x128W42: err = launch_cfg<Cfg16L42>(ta, tb, g, stream, wsrc); break;
+        case kCfg16StreamK1: err = launch_cfg<Cfg16L42S1>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x128: err = launch_cfg<Cfg16L>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x256x128: err = launch_cfg<Cfg16W>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x128W42Dl: err = launch_cfg<Cfg16L42D>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x64Kg4Dl: err = launch_cfg<Cfg16S4D>(ta, tb, g, stream, wsrc); break;
+        default: err = launch_cfg<CfgTS>(ta, tb, g, stream, wsrc); break;   // kCfgStreamK128x256
     }
+    if (wsrc.overflow) return MISGEMM_SCRATCH_TOO_SMALL;
     return err == hipSuccess ? MISGEMM_SUCCESS : MISGEMM_LAUNCH_FAILED;
 }
 
@@ -820,6 +870,12 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
 extern "C" int mi_sgemm(char transA, char transB, int M, int N, int K, float alpha, const float *A, int lda,
                         const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
     return run(-1, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+extern "C" int mi_sgemm_noalloc(char transA, char transB, int M, int N, int K, float alpha, const float *A,
+                                int lda, const float *B, int ldb, float beta, float *C, int ldc,
+                                hipStream_t stream) {
+    return run(-1, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, true);
 }
 
 extern "C" int mi_sgemm_with_config(int config, char transA, char transB, int M, int N, int K, float alpha,
@@ -881,6 +937,7 @@ extern "C" const char *mi_sgemm_status_string(int status) {
         case MISGEMM_BAD_LDC: return "ldc < max(1, N)";
         case MISGEMM_BAD_CONFIG: return "unknown kernel configuration id";
         case MISGEMM_TOO_LARGE: return "problem too large (leading dimension beyond 32-bit tile offsets, or grid too large)";
+        case MISGEMM_SCRATCH_TOO_SMALL: return "split plan needs more than the static scratch of mi_sgemm_noalloc holds";
         case MISGEMM_LAUNCH_FAILED: return "HIP kernel launch failed";
         case MISGEMM_WORKSPACE_CAPTURED: return "workspace is used by a captured HIP graph and stays allocated until the process ends";
         default: return "unknown status";

@@ -16,9 +16,11 @@
  * with double-buffered LDS) on the vector ALUs, with FP32 fused
  * multiply-adds in ascending k.
  *
- * Threading: every entry point is thread-safe. The only mutable state is the
- * set of split-K workspaces (one per device and stream, see mi_sgemm), which
- * a lock guards.
+ * Threading: every entry point is thread-safe. The only mutable host state is
+ * the set of split-K workspaces (one per device and stream, see mi_sgemm)
+ * and the per-device address of mi_sgemm_noalloc's scratch, which locks
+ * guard. Concurrent calls of mi_sgemm_noalloc on one GPU share that GPU's
+ * scratch and must not overlap (see mi_sgemm_noalloc).
  */
 #ifndef MISGEMM_H
 #define MISGEMM_H
@@ -51,6 +53,7 @@ extern "C" {
 #define MISGEMM_BAD_LDC         (-13)
 #define MISGEMM_BAD_CONFIG      (-20)
 #define MISGEMM_TOO_LARGE       (-21)
+#define MISGEMM_SCRATCH_TOO_SMALL (-22)
 #define MISGEMM_LAUNCH_FAILED     1
 #define MISGEMM_WORKSPACE_CAPTURED 2
 
@@ -94,6 +97,7 @@ extern "C" {
  * call runs unsplit). Replays use that stream's workspace: they must not
  * overlap one another or other calls on that stream, and the workspace is
  * then kept until the process ends (see mi_sgemm_release_workspace).
+ * mi_sgemm_noalloc captures without any prior call.
  *
  * Alignment: any pointer and leading dimension is accepted. 16-byte aligned
  * pointers with lda, ldb, ldc multiples of 4 take the dwordx4 path.
@@ -158,6 +162,39 @@ const char *mi_sgemm_status_string(int status);
  * stream.
  */
 int mi_sgemm_release_workspace(hipStream_t stream);
+
+/*
+ * mi_sgemm_noalloc: mi_sgemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops that forbid allocation). Same
+ * arguments, kernels, results and errors as mi_sgemm, but it never calls
+ * hipMalloc or hipFree: the split-K, stream-K and skinny-band kernels keep
+ * their partial blocks and tile counters in a static device array of the
+ * library (scratch) instead of a per-stream workspace.
+ *
+ * Scratch: 64 MiB of partial blocks and 65,536 tile counters (256 KiB), the
+ * same capacity as a stream's workspace, so the same split plan and the same
+ * bits as mi_sgemm. Each GPU the library runs this entry point on holds its
+ * own copy until the process ends (the device memory is reserved when the
+ * library's code object is loaded on that GPU). The split plans are bounded
+ * by this capacity; a plan that would exceed it is refused with
+ * MISGEMM_SCRATCH_TOO_SMALL and nothing is enqueued.
+ *
+ * The first call on a device looks up that device's copy of the array
+ * (hipGetSymbolAddress) and, unless the stream is being captured, clears its
+ * counters with a kernel on `stream`; the loader hands the array over
+ * zero-filled, and every split product leaves its counters at zero.
+ *
+ * Concurrency: every call on one GPU shares that GPU's scratch. Calls that
+ * may overlap on one GPU -- on different streams, from different threads, or
+ * replays of graphs that captured this call -- race on the partial blocks
+ * and counters and give wrong results; order them (one stream, or events).
+ * The scratch keeps the last call's contents; nothing is read before this
+ * call has written it.
+ */
+int mi_sgemm_noalloc(char transA, char transB, int M, int N, int K,
+                     float alpha, const float *A, int lda,
+                     const float *B, int ldb,
+                     float beta, float *C, int ldc, hipStream_t stream);
 
 #ifdef __cplusplus
 }
