@@ -7,11 +7,29 @@ srand48(4)); inputs are resident in HBM before timing starts. The FLOP
 count 2MNK is the convention of the klklkl10086.github.io SGEMM page
 (problem definition), where 4096^3 is 137.4 GFLOP.
 
+Before the warm-up steps, back-to-back calls run for --preheat seconds
+(default 1): the GPU raises its shader clock over the first ~20 ms of load
+and drops it again after about a second idle, so without this the timed
+steps would measure the ramp. The preheat is reported in its own field.
+
 Prints one JSON line. Besides the contract fields it carries
+  preheat       calls and seconds of the preheat;
+  per_call_us   median, min, p90, max, first and last of the timed steps, each
+                step bracketed by its own HIP events;
   roofline      the SGEMM kernel against the FP32 matrix-core peak, with the
                 average launch time measured by HIP events on the launch stream,
                 and HBM traffic from the committed rocprofv3 counter summary
                 when that summary was taken on the current kernel source;
+  clock         the shader clock sustained under full FP32 matrix load
+                (mi_clock_probe, run right after the timed steps), the
+                matrix rate the probe reached, and the fraction of the peak
+                at that clock;
+  check         the headline C at 4,096 seeded positions against the CPU
+                oracle (max |GPU - oracle| <= 1e-3; the run fails otherwise);
+  configs       every workload family (the ragged, 1024^3, square sweep,
+                layer-shaped and skinny products), each preheated, timed
+                back to back (and one call at a time from 20 us up), and
+                checked at sampled positions against the oracle;
   cpu_baseline  the CPU oracle timed on this host on a bounded sample.
 
 Other modes: --table writes per-workload TFLOPS (and GB/s for the skinny
@@ -98,6 +116,59 @@ class Problem:
         rc = mg.mi_sgemm(*args) if config is None else mg.mi_sgemm_with_config(config, *args)
         if rc != 0:
             raise RuntimeError(f"mi_sgemm: {mg.mi_sgemm_status_string(rc)}")
+
+
+def preheat(prob, seconds, config=None):
+    """Back-to-back calls for `seconds` of wall time (at least one batch of
+    about 10 ms), so that the shader clock has ramped before anything is timed.
+    Returns the call count and the time spent."""
+    import torch
+
+    handle = torch.cuda.current_stream().cuda_stream
+    t0 = time.perf_counter()
+    calls, batch = 0, 4
+    while True:
+        tb = time.perf_counter()
+        for i in range(batch):
+            prob.call(calls + i, handle, config)
+        torch.cuda.synchronize()
+        calls += batch
+        dt = time.perf_counter() - tb
+        if time.perf_counter() - t0 >= seconds:
+            break
+        batch = max(1, min(2000, int(batch * 0.01 / max(dt, 1e-6))))
+    return {"calls": calls, "seconds": round(time.perf_counter() - t0, 3)}
+
+
+def time_steps(prob, steps, warmup, config=None):
+    """`warmup` untimed calls, then exactly `steps` calls bracketed by
+    synchronisations, with a HIP event on the launch stream before the first
+    call and after each one. Returns the wall time, the event time from the
+    first event to the last (seconds) and each step's event time (us)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    for i in range(warmup):
+        prob.call(i, handle, config)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        prob.call(i, handle, config)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]
+    return wall, ev[0].elapsed_time(ev[steps]) / 1e3, per
+
+
+def spread(per_us):
+    """Median, min, 90th percentile, max, first and last of per-call times."""
+    t = sorted(per_us)
+    return {"median": round(t[len(t) // 2], 2), "min": round(t[0], 2), "p90": round(t[(len(t) * 9) // 10], 2),
+            "max": round(t[-1], 2), "first": round(per_us[0], 2), "last": round(per_us[-1], 2)}
 
 
 def time_problem(prob, steps, warmup, config=None):
@@ -193,6 +264,138 @@ def cpu_baseline(case, min_seconds=10.0, max_seconds=30.0):
               f"{reps} x first {rows} rows of the {case.M}x{case.N}x{case.K} {case.transA}{case.transB} product")
     return {"value": round(tflops(flops, spent), 6), "unit": "TFLOPS", "cores": threads,
             "kind": "oracle", "sample": sample, "seconds": round(spent, 2)}
+
+
+CHECK_TOL = 1e-3
+
+
+def check_sampled(prob, samples, seed, reset=True):
+    """The result of one call against the CPU oracle at `samples` seeded
+    positions (the four corners among them): max |GPU - oracle|. With `reset`
+    C is first restored to C_in and one call is made, so a C that repeated
+    timing calls have drifted (beta != 0) is not what is checked."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    case, inp = prob.case, prob.inp
+    A, B, C = prob.sets[0]
+    if reset:
+        C.copy_(torch.from_numpy(inp.C))
+        torch.cuda.synchronize()
+        prob.call(0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got_all = C.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([[0, 0, case.M - 1, case.M - 1], rng.integers(0, case.M, samples - 4)]).astype(np.int32)
+    cols = np.concatenate([[0, case.N - 1, 0, case.N - 1], rng.integers(0, case.N, samples - 4)]).astype(np.int32)
+    c_in = inp.C[rows, cols] if case.beta != 0.0 else None
+    want = oracle.sgemm_entries(case.transA, case.transB, case.M, case.N, case.K, case.alpha, inp.A, case.lda_,
+                                inp.B, case.ldb_, case.beta, c_in, rows, cols)
+    got = got_all[rows, cols]
+    finite = bool(np.all(np.isfinite(got)))
+    err = float(np.abs(got.astype(np.float64) - want.astype(np.float64)).max())
+    return {"samples": int(samples), "max_abs_err": err, "tol": CHECK_TOL, "pass": finite and err <= CHECK_TOL}
+
+
+PROBE_ITERS = 100_000     # about 20 ms per launch at 2.4 GHz
+PROBE_WORKGROUPS, PROBE_WAVES = 256, 8
+
+
+def clock_probe():
+    """Shader clock under full FP32 matrix load (mi_clock_probe): three
+    back-to-back launches, the last one read. Returns the median shader clock
+    over the workgroups, the matrix rate the probe reached (FLOPs over the
+    longest wall span) and the FP32 matrix peak at the measured clock."""
+    import torch
+
+    import fp32_gemm_nn_amd as mg
+
+    stamps = torch.zeros(4 * PROBE_WORKGROUPS, dtype=torch.int64, device="cuda")
+    handle = torch.cuda.current_stream().cuda_stream
+    khz = 0
+    for _ in range(3):
+        rc, khz = mg.mi_clock_probe(PROBE_ITERS, stamps.data_ptr(), handle)
+        if rc != 0:
+            raise RuntimeError(f"mi_clock_probe: {mg.mi_sgemm_status_string(rc)}")
+    torch.cuda.synchronize()
+    st = stamps.cpu().tolist()
+    clk = [st[4 * w + 1] - st[4 * w] for w in range(PROBE_WORKGROUPS)]
+    wall = [st[4 * w + 3] - st[4 * w + 2] for w in range(PROBE_WORKGROUPS)]
+    mhz = sorted(c / w * khz / 1e3 for c, w in zip(clk, wall) if w > 0)
+    sclk = mhz[len(mhz) // 2]
+    flops = PROBE_WORKGROUPS * PROBE_WAVES * PROBE_ITERS * 4 * 4096
+    probe_tflops = flops / (max(wall) / (khz * 1e3)) / 1e12
+    peak_at_sclk = 256 * 256 * sclk * 1e6 / 1e12
+    return {"sclk_mhz": round(sclk, 1), "sclk_mhz_min": round(mhz[0], 1), "sclk_mhz_max": round(mhz[-1], 1),
+            "wall_clock_khz": khz, "probe_tflops": round(probe_tflops, 2),
+            "peak_at_sclk_tflops": round(peak_at_sclk, 2),
+            "source": "mi_clock_probe: 256 workgroups x 8 waves of register-only FP32 MFMA, after the timed steps"}
+
+
+def time_case(case, copies=1, preheat_s=0.1, check_samples=512, seed=0):
+    """One workload with its chosen kernel: preheated, then timed as five
+    batches of back-to-back calls (each batch at least 2 ms, one HIP event
+    pair around it); `us` is the median of the five batch means, the time per
+    call at full throughput, as the headline's roofline time is. Calls of 20 us
+    or more are also timed one by one (`per_call_us`: an event pair around each
+    call, which adds the dispatch gap between calls). Then one call on a fresh
+    C is checked against the oracle at sampled positions."""
+    import torch
+
+    import fp32_gemm_nn_amd as mg
+
+    prob = Problem(case, copies=copies)
+    ph = preheat(prob, preheat_s)
+    stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream
+    est = ph["seconds"] / max(ph["calls"], 1)
+    reps = max(5, min(2000, int(2e-3 / max(est, 1e-7))))
+    means = []
+    for b in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            prob.call(b * reps + i, handle)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        means.append(e0.elapsed_time(e1) * 1e3 / reps)
+    us = sorted(means)[2]
+    tf = tflops(case.flops, us * 1e-6)
+    row = {"workload": case.name, "ops": case.transA + case.transB, "M": case.M, "N": case.N, "K": case.K,
+           "alpha": case.alpha, "beta": case.beta,
+           "kernel_config": mg.mi_sgemm_config_name(
+               mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)),
+           "us": round(us, 2), "calls_per_batch": reps, "TFLOPS": round(tf, 2),
+           "pct_fp32_matrix_peak": round(100 * tf / PEAK_FP32_MATRIX_TFLOPS, 2)}
+    if us >= 20:
+        _, _, per = time_steps(prob, max(20, min(200, int(0.05 / (us * 1e-6)))), 2)
+        row["per_call_us"] = spread(per)
+    if case.M <= 32:
+        gbps = case.algorithmic_bytes / (us * 1e-6) / 1e9
+        row.update({"GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+                    "operand_sets": copies})
+    chk = check_sampled(prob, check_samples, seed)
+    row["check_max_abs_err"] = chk["max_abs_err"]
+    row["check_pass"] = chk["pass"]
+    del prob
+    return row
+
+
+def run_configs():
+    """Every workload family of the benchmark, in the order C1, C2, the square
+    sweep, the layer-shaped products, the skinny product (cold: eight operand
+    sets, more than the 256 MB last-level cache; warm: one)."""
+    from synthetic import workloads as W
+
+    out = {"C1": time_case(W.C1, seed=1), "C2": time_case(W.C2, seed=2),
+           "C3": [time_case(W.c3(n), seed=3) for n in W.C3_SIZES],
+           "C5a": [time_case(c, seed=5) for c in W.C5A]}
+    cold = time_case(W.C5B, copies=8, seed=6)
+    warm = time_case(W.C5B, copies=1, seed=7)
+    out["C5b"] = {"cold": cold, "warm": warm}
+    return out
 
 
 def host_info():
@@ -448,6 +651,10 @@ def main():
     ap.add_argument("--mode", choices=["gemm", "copy"], default="gemm")
     ap.add_argument("--table", metavar="PATH", help="also write per-workload numbers to PATH")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--preheat", type=float, default=1.0,
+                    help="seconds of back-to-back calls before the warm-up steps (reported as `preheat`)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other workload families (the `configs` field)")
     ap.add_argument("--sweep-configs", metavar="PATH",
                     help="also time every kernel configuration on every workload, to PATH")
     ap.add_argument("--config", action="append", metavar="NAME_OR_ID",
@@ -498,11 +705,15 @@ def main():
 
     case = W.HEADLINE
     prob = Problem(case)
-    wall, ev = time_problem(prob, args.steps, args.warmup)
+    heat = preheat(prob, args.preheat)
+    wall, ev, per = time_steps(prob, args.steps, args.warmup)
+    clock = clock_probe()
     flops = case.flops
     value = tflops(flops * args.steps, wall)
     per_launch = ev / args.steps
     achieved = tflops(flops, per_launch)
+    clock["pct_of_peak_at_sclk"] = round(100 * achieved / clock["peak_at_sclk_tflops"], 2)
+    check = check_sampled(prob, 4096, seed=4, reset=False)
     traffic = load_traffic(case.name)
     cfg_id = mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)
     result = {
@@ -512,6 +723,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "preheat": heat,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -537,9 +749,15 @@ def main():
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": case.algorithmic_bytes,
         },
+        "per_call_us": spread(per),
+        "clock": clock,
+        "check": check,
+        "configs": None,
         "cpu_baseline": None,
     }
     del prob
+    if not args.no_configs:
+        result["configs"] = run_configs()
     if args.table:
         run_table(args.table, 20, 5)
     if args.sweep_configs:
@@ -549,6 +767,14 @@ def main():
         cb.update(host_info())
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
+    bad = [] if check["pass"] else ["headline"]
+    if result["configs"]:
+        c = result["configs"]
+        rows = [c["C1"], c["C2"], *c["C3"], *c["C5a"], c["C5b"]["cold"], c["C5b"]["warm"]]
+        bad += [r["workload"] for r in rows if not r["check_pass"]]
+    if bad:
+        print(f"bench.py: result check failed for {', '.join(bad)}", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -19,7 +19,7 @@ __all__ = [
     "MisgemmError", "library_path", "load_library",
     "mi_sgemm", "mi_sgemm_noalloc", "mi_sgemm_with_config", "mi_sgemm_select_config",
     "mi_sgemm_config_count", "mi_sgemm_config_name", "mi_sgemm_status_string",
-    "mi_sgemm_release_workspace", "sgemm", "config_names",
+    "mi_sgemm_release_workspace", "mi_clock_probe", "sgemm", "config_names",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,8 @@ def load_library():
     lib.mi_sgemm_status_string.restype = ctypes.c_char_p
     lib.mi_sgemm_release_workspace.argtypes = [p]
     lib.mi_sgemm_release_workspace.restype = i
+    lib.mi_clock_probe.argtypes = [i, p, ctypes.POINTER(i), p]
+    lib.mi_clock_probe.restype = i
     _lib = lib
     return lib
 
@@ -120,6 +122,14 @@ def mi_sgemm_status_string(status) -> str:
 def mi_sgemm_release_workspace(stream=0) -> int:
     """C ABI mi_sgemm_release_workspace (integer stream handle); returns the status code."""
     return load_library().mi_sgemm_release_workspace(stream or None)
+
+
+def mi_clock_probe(iters, stamps, stream=0):
+    """C ABI mi_clock_probe (measurement aid): enqueue the probe writing to the
+    device buffer `stamps` (int address); returns (status, wall_clock_khz)."""
+    khz = ctypes.c_int(0)
+    rc = load_library().mi_clock_probe(int(iters), stamps or None, ctypes.byref(khz), stream or None)
+    return rc, khz.value
 
 
 def config_names() -> list[str]:

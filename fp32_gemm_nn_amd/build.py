@@ -13,7 +13,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", name) for name in ("misgemm.hip", "ladder.hip", "scratch.hip")]
+SRCS = [os.path.join(PKG, "csrc", name) for name in ("misgemm.hip", "ladder.hip", "scratch.hip", "clock_probe.hip")]
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmisgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

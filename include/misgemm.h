@@ -196,6 +196,28 @@ int mi_sgemm_noalloc(char transA, char transB, int M, int N, int K,
                      const float *B, int ldb,
                      float beta, float *C, int ldc, hipStream_t stream);
 
+/*
+ * mi_clock_probe: measurement aid, not part of the product path. Reads the
+ * shader clock the GPU sustains under full FP32 matrix load, so that a
+ * kernel time can be stated beside the clock it ran at (the klklkl10086
+ * SGEMM page, "【CUDA】Sgemm单精度矩阵乘法", 00-朴素实现, prints the SM
+ * frequency in its Speed Of Light table beside each duration).
+ *
+ * Enqueues one kernel on `stream`: 256 workgroups (one per CU) of eight
+ * waves, each wave issuing `iters` rounds of four independent
+ * v_mfma_f32_32x32x2_f32 (4096 FLOP each) on registers only. Wave 0 of
+ * workgroup w writes four values to stamps[4w .. 4w+3]: the shader-clock
+ * counter before and after the loop, then the constant-rate wall clock
+ * before and after. `stamps` is a device buffer of at least 1024 unsigned
+ * 64-bit integers owned by the caller. If `wall_clock_khz` is not NULL it
+ * receives the wall clock's rate (kHz) for the stream's device (the current
+ * device for the null stream). Shader clock = (c1 - c0) / (w1 - w0) * rate;
+ * the matrix rate reached is 256 * 8 * iters * 4 * 4096 FLOP over the
+ * longest wall span. Returns MISGEMM_BAD_M for iters < 0, MISGEMM_NULL_C for
+ * a null `stamps`, MISGEMM_LAUNCH_FAILED if a HIP call fails.
+ */
+int mi_clock_probe(int iters, unsigned long long *stamps, int *wall_clock_khz, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

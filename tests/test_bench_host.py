@@ -89,3 +89,10 @@ def test_committed_traffic_summary_is_for_the_headline_workload():
     assert t["algorithmic_bytes_per_launch"] == W.HEADLINE.algorithmic_bytes
     # Read and write bytes, each a copy-calibrated counter reading, add up.
     assert t["hbm_bytes_per_launch"] == t["hbm_read_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
+
+
+def test_spread_of_per_call_times():
+    per = [5.0, 1.0, 4.0, 2.0, 3.0, 9.0, 7.0, 8.0, 6.0, 10.0]
+    s = bench.spread(per)
+    assert s == {"median": 6.0, "min": 1.0, "p90": 10.0, "max": 10.0, "first": 5.0, "last": 10.0}
+    assert bench.spread([2.5]) == {"median": 2.5, "min": 2.5, "p90": 2.5, "max": 2.5, "first": 2.5, "last": 2.5}
