@@ -447,13 +447,55 @@ int select_config(char transA, char transB, int M, int N, int K) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Whether the tile has a 4-byte straight-line instantiation for this op pair:
+// every clamping tile, except the forms whose clamped element addresses do
+// not fit the register budget (they spilled: the 128 x 256 x 16 tile, the
+// two-workgroup stream-K tile, the 16 x 16 128 x 128 w4x2 tile other than NT,
+// and the 32 x 32 128 x 128 w2x4 / w4x2 tiles for TN). mi_sgemm routes
+// operands without 16-byte loads away from these tiles (unaligned_substitute);
+// when one is forced, it runs the guarded rounds.
+template <class CFG, bool TA, bool TB>
+constexpr bool kScalarForm =
+    kClampEdge<CFG> && !std::is_same_v<CFG, CfgT16> && !std::is_same_v<CFG, CfgL42S2> &&
+    !(std::is_same_v<CFG, Cfg16L42> && !(!TA && TB)) &&
+    !((std::is_same_v<CFG, CfgL24> || std::is_same_v<CFG, CfgL42>) && TA && !TB);
+
+// Operands that cannot be read with 16-byte loads: the pick for aligned ones
+// replaced by a tile whose 4-byte straight-line rounds exist. The 256 x 256
+// tiles have none (4096 x 4096 x 4095 NN: 1003 us on 256 x 128 against 1245;
+// TT on 128 x 256: 1006 against 1253); for the others the replacement was the
+// fastest measured (MI355X, pointers one float off 16 bytes):
+//   128 x 256 x 16 -> 256 x 128 / 128 x 256   (4000^3 NN: 982 us vs 1046)
+//   two-workgroup stream-K -> 16 x 16 stream-K (2304 x 2304 x 1024 NT: 97.9 vs
+//                                              106.0 us; TT: 106.2 vs 117.4)
+//   16 x 16 128 x 128 w4x2 (not NT) -> 256 x 128 on a grid it fills evenly
+//                                     (2048 x 4096 x 1024 NN / TN / TT: 136 /
+//                                     145 / 139 us vs 153 / 174 / 176), else
+//                                     the 16 x 16 stream-K tile (2048^3 NN:
+//                                     148.5 vs 151.1 us)
+int unaligned_substitute(int config, bool ta, bool tb, int M, int N) {
+    const bool wide = M < N;
+    auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    switch (config) {
+        case kCfg256x256:
+        case kCfg256x256Dl: return (ta && tb) ? kCfg128x256 : kCfg256x128;
+        case kCfg128x256x16: return wide && !(ta && tb) ? kCfg128x256 : kCfg256x128;
+        case kCfgStreamK2: return kCfg16StreamK1;
+        case kCfg16x128W42:
+            if (!ta && tb) return config;
+            return (tiles(256, 128) >= kNumCus && cu_balance(tiles(256, 128)) >= 0.9) ? kCfg256x128
+                                                                                        : kCfg16StreamK1;
+        default: return config;
+    }
+}
+
 template <class CFG, bool TA, bool TB>
 hipError_t launch_t(const GemmArgs &g, unsigned workgroups, hipStream_t stream) {
     dim3 grid(workgroups);
     dim3 block(CFG::NT);
     // Operands without 16-byte loads: the 4-byte straight-line instantiation
     // where the tile has one, else the guarded rounds of the usual kernel.
-    if constexpr (kClampEdge<CFG>) {
+    if constexpr (kScalarForm<CFG, TA, TB>) {
         if (!g.vec_ab) {
             hipLaunchKernelGGL((sgemm_mfma32<CFG, TA, TB, true>), grid, block, 0, stream, g);
             return hipGetLastError();
@@ -780,12 +822,7 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
     const bool ta = op_t(transA), tb = op_t(transB);
     if (config < 0) {
         config = select_config(transA, transB, M, N, K);
-        // The 256 x 256 tile has no straight-line rounds for operands without
-        // 16-byte loads; the 256 x 128 / 128 x 256 tiles have (4096 x 4096 x
-        // 4095 NN: 1003 us on 256 x 128 against 1245; TT on 128 x 256: 1006
-        // against 1253).
-        if (!g.vec_ab && (config == kCfg256x256 || config == kCfg256x256Dl))
-            config = (ta && tb) ? kCfg128x256 : kCfg256x128;
+        if (!g.vec_ab) config = unaligned_substitute(config, ta, tb, M, N);
     }
     if ((config == kCfgSkinny16 || config == kCfgBand) && (M + 2 * 16 - 1) / (2 * 16) > 65535)
         return MISGEMM_TOO_LARGE;

@@ -62,6 +62,11 @@ struct TileCfg {
     // DL: the straight-line rounds move tiles global -> LDS directly
     // (global_load_lds_dwordx4), with unpadded, chunk-swizzled LDS rows.
     static constexpr bool DL = DL_;
+    // SWZ: LDS rows unpadded, k-contiguous tiles chunk-swizzled (the layout
+    // direct loads need), whether the tiles arrive directly or through
+    // registers. 16 x 16 blocks use it: their fragment reads conflict on the
+    // padded rows and not on these.
+    static constexpr bool SWZ = DL_ || MI16_;
     // SPLIT: the kernel carries the split-K-over-workgroups reduction.
     static constexpr bool SPLIT = SPLIT_;
     // STREAMK: one workgroup per CU walks an equal share of all (tile,
@@ -103,21 +108,22 @@ template <> struct LdsVec<4> {
 // LDS in 16-byte chunks. Thread t handles chunks t, t+NT, ...; a chunk is four
 // consecutive columns of one row. LDS layout: [R][CC + kLdsPad].
 //
-// DL layout (for direct global -> LDS loads, which write a wave's 64 chunks
-// to 1 KB of consecutive LDS): rows are unpadded, [R][CC]. When SWZ (a
-// k-contiguous tile, read as 16-byte runs down 8 consecutive rows), chunk c
-// of row r sits at chunk position c ^ swz(r) -- r mod 8 for rows of 8 or
-// more chunks, (r / 2) mod 4 for rows of 4 -- so those 8 reads fall on 8
-// different 16-byte bank groups, as the padding achieves otherwise.
-template <int R, int CC, int NT, bool DL = false, bool SWZ = false>
+// Unpadded layout (UNPAD; required for direct global -> LDS loads, which
+// write a wave's 64 chunks to 1 KB of consecutive LDS): rows are [R][CC].
+// When SWZ (a k-contiguous tile, read as 16-byte runs down 8 consecutive
+// rows), chunk c of row r sits at chunk position c ^ swz(r) -- r mod 8 for
+// rows of 8 or more chunks, (r / 2) mod 4 for rows of 4 -- so those 8 reads
+// fall on 8 different 16-byte bank groups, as the padding achieves otherwise.
+template <int R, int CC, int NT, bool DL = false, bool SWZ = false, bool UNPAD = DL>
 struct TileCopy {
     static constexpr int CPR = CC / 4;                  // chunks per row
     static constexpr int CHUNKS = R * CPR;
     static constexpr int PER_THREAD = CHUNKS / NT;
-    static constexpr int STRIDE = DL ? CC : CC + kLdsPad;
+    static constexpr int STRIDE = UNPAD ? CC : CC + kLdsPad;
     static constexpr int LDS_FLOATS = R * STRIDE;
     static_assert(CC % 4 == 0 && CHUNKS % NT == 0, "tile must split evenly over the threads");
-    static_assert(!SWZ || (DL && (CPR == 4 || CPR % 8 == 0)), "swizzle is for 16-wide or multiple-of-32-wide k-contiguous rows");
+    static_assert(!DL || UNPAD, "direct loads fill unpadded rows");
+    static_assert(!SWZ || (UNPAD && (CPR == 4 || CPR % 8 == 0)), "swizzle is for unpadded 16-wide or multiple-of-32-wide k-contiguous rows");
     static_assert(!DL || NT % 64 == 0, "direct loads are issued per wave");
 
     // Chunk position of chunk c in row r (SWZ), and its LDS float offset.

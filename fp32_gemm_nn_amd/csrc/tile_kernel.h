@@ -36,9 +36,11 @@ struct Frag {
         }
     }
 
-    // as/bs: LDS tiles of one k-tile, row strides AS/BS.
+    // as/bs: LDS tiles of one k-tile, row strides AS/BS (lds0, the start of
+    // the workgroup's LDS, is not needed by this layout).
     template <int AS, int BS>
-    __device__ __forceinline__ void read(const float *as, const float *bs, int q, int wm, int wn, int li, int lh) {
+    __device__ __forceinline__ void read(const float *, const float *as, const float *bs, int q, int wm, int wn,
+                                         int li, int lh) {
         if (!TA) {
             // k-contiguous A tile [m][k]: block blk, lane row li is m = 32*blk + li.
 #pragma unroll
@@ -98,24 +100,47 @@ struct Frag16 {
     float b[FN][4];
 
     // Float offset of the lane's four k values inside a k-contiguous LDS row
-    // (row c plus a multiple of 16), at its swizzled chunk position in the DL
-    // layout.
+    // (row c plus a multiple of 16), at its swizzled chunk position in the
+    // unpadded layout.
     static __device__ __forceinline__ int kofs(int c, int g, int q) {
-        if constexpr (CFG::DL) {
+        if constexpr (CFG::SWZ) {
             return ((4 * q + g) ^ (c & 7)) * 4;
         } else {
             return 16 * q + 4 * g;
         }
     }
 
-    // c, g: the lane's column and group (lane % 16, lane / 16).
+    // The lane's 16-byte k-run for q-group q in row `row` of a k-contiguous
+    // tile. Swizzled rows are 32 floats per 8 chunks, and every tile buffer
+    // starts a whole number of rows into `lds0`, so an odd q-group's run is
+    // the even one's with float-offset bit 4 flipped: formed with one XOR at
+    // the read rather than held as a second address across the k-loop (the
+    // offset from lds0 includes the round's buffer, so it is not hoisted).
+    // Rows 16 apart (the next block) keep the same chunk position, so adding
+    // 16 rows after the flip is exact.
+    template <int STRIDE>
+    static __device__ __forceinline__ const float *krun(const float *lds0, const float *tile, int row, int c, int g,
+                                                          int q) {
+        if constexpr (CFG::SWZ) {
+            static_assert(STRIDE % 32 == 0, "swizzled rows hold whole groups of 8 chunks");
+            const float *p = tile + row * STRIDE + kofs(c, g, q & ~1);
+            return (q & 1) ? lds0 + ((int)(p - lds0) ^ 16) : p;
+        } else {
+            return tile + row * STRIDE + kofs(c, g, q);
+        }
+    }
+
+    // c, g: the lane's column and group (lane % 16, lane / 16); lds0: the
+    // start of the workgroup's LDS, which the tiles lie in.
     template <int AS, int BS>
-    __device__ __forceinline__ void read(const float *as, const float *bs, int q, int wm, int wn, int c, int g) {
+    __device__ __forceinline__ void read(const float *lds0, const float *as, const float *bs, int q, int wm, int wn,
+                                         int c, int g) {
         const int k0 = 16 * q + 4 * g;
         if (!TA) {
+            // Blocks are 16 rows apart: one address, immediate offsets.
+            const float *pa = krun<AS>(lds0, as, wm * WTM + c, c, g, q);
 #pragma unroll
-            for (int blk = 0; blk < FM; ++blk)
-                LdsVec<4>::get(as + (wm * WTM + 16 * blk + c) * AS + kofs(c, g, q), a[blk]);
+            for (int blk = 0; blk < FM; ++blk) LdsVec<4>::get(pa + 16 * blk * AS, a[blk]);
         } else {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -126,9 +151,9 @@ struct Frag16 {
             }
         }
         if (TB) {
+            const float *pb = krun<BS>(lds0, bs, wn * WTN + c, c, g, q);
 #pragma unroll
-            for (int blk = 0; blk < FN; ++blk)
-                LdsVec<4>::get(bs + (wn * WTN + 16 * blk + c) * BS + kofs(c, g, q), b[blk]);
+            for (int blk = 0; blk < FN; ++blk) LdsVec<4>::get(pb + 16 * blk * BS, b[blk]);
         } else {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -223,8 +248,8 @@ void sgemm_mfma32(GemmArgs g) {
     static_assert(Q % 2 == 0, "fragment buffers alternate, so the q-group count must be even");
     // Stored tile shapes: A is BM x BK ('N', k contiguous) or BK x BM ('T',
     // m contiguous); B is BK x BN ('N', n contiguous) or BN x BK ('T').
-    using ACopy = TileCopy<TA ? BK : BM, TA ? BM : BK, NTG, CFG::DL, CFG::DL && !TA>;
-    using BCopy = TileCopy<TB ? BN : BK, TB ? BK : BN, NTG, CFG::DL, CFG::DL && TB>;
+    using ACopy = TileCopy<TA ? BK : BM, TA ? BM : BK, NTG, CFG::DL, CFG::SWZ && !TA, CFG::SWZ>;
+    using BCopy = TileCopy<TB ? BN : BK, TB ? BK : BN, NTG, CFG::DL, CFG::SWZ && TB, CFG::SWZ>;
     using F = std::conditional_t<CFG::MI16, Frag16<CFG, TA, TB>, Frag<CFG, TA, TB>>;
     constexpr int A_FLOATS = ACopy::LDS_FLOATS, B_FLOATS = BCopy::LDS_FLOATS;
     constexpr int AS = ACopy::STRIDE, BS = BCopy::STRIDE;
@@ -309,10 +334,15 @@ void sgemm_mfma32(GemmArgs g) {
             // left fast without edge clamping), the rest guarded. Rows/cols
             // left counted from this k-tile's origin.
             const bool guard = CLAMP_EDGE || !(wg_fast && kt < kfull);
+            // Tiles that clamp their edges reach this only for the k-tail
+            // round: with the thread id made opaque here its element addresses
+            // are formed when needed instead of being held through the k-loop.
+            int ltid = gtid;
+            if constexpr (CLAMP_EDGE) asm volatile("" : "+v"(ltid));
             ca.load(a_ptr + kt * a_step, g.lda, TA ? a_rows - k0 : a_rows, TA ? a_cols : a_cols - k0, guard,
-                    vec, gtid);
+                    vec, ltid);
             cb.load(b_ptr + kt * b_step, g.ldb, TB ? b_rows : b_rows - k0, TB ? b_cols - k0 : b_cols, guard,
-                    vec, gtid);
+                    vec, ltid);
         };
 
         AccT acc[FM][FN];
@@ -334,7 +364,7 @@ void sgemm_mfma32(GemmArgs g) {
             cb.store(b_lds, gtid);
         }
         __syncthreads();
-        if (kt_begin + grp < kt_end) f0.template read<AS, BS>(a_lds, b_lds, 0, wm, wn, li, lh);
+        if (kt_begin + grp < kt_end) f0.template read<AS, BS>(lds, a_lds, b_lds, 0, wm, wn, li, lh);
 
         // Straight-line rounds (this and the next k-tile complete and in
         // range) first, then the guarded ones, as two loops; the condition
@@ -359,10 +389,10 @@ void sgemm_mfma32(GemmArgs g) {
                 }
 #pragma unroll
                 for (int q = 0; q < Q; q += 2) {
-                    f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
+                    f1.template read<AS, BS>(lds, as, bs, q + 1, wm, wn, li, lh);
                     f0.mma(acc);
                     if (q + 2 < Q) {
-                        f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
+                        f0.template read<AS, BS>(lds, as, bs, q + 2, wm, wn, li, lh);
                     } else if constexpr (!CFG::DL) {
                         ca.store(as_n, gtid);
                         cb.store(bs_n, gtid);
@@ -379,7 +409,7 @@ void sgemm_mfma32(GemmArgs g) {
                 // Direct loads complete (vmcnt) before the barrier publishes them.
                 if constexpr (CFG::DL) __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
-                f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
+                f0.template read<AS, BS>(lds, as_n, bs_n, 0, wm, wn, li, lh);
             }
         }
         for (; r < rounds; ++r) {
@@ -394,9 +424,9 @@ void sgemm_mfma32(GemmArgs g) {
             if (has_cur) {
 #pragma unroll
                 for (int q = 0; q < Q; q += 2) {
-                    f1.template read<AS, BS>(as, bs, q + 1, wm, wn, li, lh);
+                    f1.template read<AS, BS>(lds, as, bs, q + 1, wm, wn, li, lh);
                     f0.mma(acc);
-                    if (q + 2 < Q) f0.template read<AS, BS>(as, bs, q + 2, wm, wn, li, lh);
+                    if (q + 2 < Q) f0.template read<AS, BS>(lds, as, bs, q + 2, wm, wn, li, lh);
                     f1.mma(acc);
                 }
             }
@@ -405,7 +435,7 @@ void sgemm_mfma32(GemmArgs g) {
                 cb.store(bs_n, gtid);
             }
             __syncthreads();
-            if (has_next) f0.template read<AS, BS>(as_n, bs_n, 0, wm, wn, li, lh);
+            if (has_next) f0.template read<AS, BS>(lds, as_n, bs_n, 0, wm, wn, li, lh);
         }
 
         if constexpr (KG > 1) {

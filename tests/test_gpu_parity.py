@@ -369,13 +369,26 @@ def test_clamped_edge_tiles(config, ta, tb, layout):
         compare(case, got, want, True)
 
 
-@pytest.mark.parametrize("ta,tb,M,N,K,layout", [("N", "N", 4096, 4096, 2048, "offset"),
-                                                 ("T", "T", 4096, 4096, 1024, "odd_ld")])
-def test_unaligned_operands_on_256x256_shapes(ta, tb, M, N, K, layout):
-    """Shapes whose pick for 16-byte-loadable operands is a 256 x 256 tile:
-    with unaligned operands mi_sgemm runs a 256 x 128 or 128 x 256 tile
-    instead (4-byte straight-line rounds). Bit-exact on integer inputs."""
-    assert "256x256" in mg.config_names()[mg.mi_sgemm_select_config(ta, tb, M, N, K)]
+@pytest.mark.parametrize("ta,tb,M,N,K,layout,aligned_pick", [
+    ("N", "N", 4096, 4096, 2048, "offset", "mfma32_256x256x32_w4x2"),
+    ("T", "T", 4096, 4096, 1024, "odd_ld", "mfma32_256x256x32_w4x2_dl"),
+    ("N", "N", 4000, 4000, 4000, "offset", "mfma32_128x256x16_w2x2"),
+    ("T", "N", 4000, 4000, 2000, "odd_ld", "mfma32_128x256x16_w2x2"),
+    ("N", "T", 2304, 2304, 1024, "offset", "mfma32_128x128x32_w4x2_streamk_2wg"),
+    ("T", "T", 2304, 2304, 1024, "odd_ld", "mfma32_128x128x32_w4x2_streamk_2wg"),
+    ("N", "N", 2048, 4096, 1024, "offset", "mfma16_128x128x32_w4x2"),
+    ("T", "N", 2048, 4096, 1024, "odd_ld", "mfma16_128x128x32_w4x2"),
+    ("T", "T", 2048, 4096, 1024, "offset", "mfma16_128x128x32_w4x2"),
+    ("N", "T", 2048, 4096, 1024, "offset", "mfma16_128x128x32_w4x2"),
+    ("N", "N", 2000, 2000, 2001, "odd_ld", "mfma16_128x128x32_w4x2"),
+])
+def test_unaligned_operands_on_substituted_tiles(ta, tb, M, N, K, layout, aligned_pick):
+    """Shapes whose pick for 16-byte-loadable operands is a tile without a
+    4-byte straight-line form for that op pair (the 256 x 256 and
+    128 x 256 x 16 tiles, the two-workgroup stream-K tile, the 16 x 16
+    128 x 128 w4x2 tile except NT): with unaligned operands mi_sgemm runs a
+    substitute with 4-byte straight-line rounds. Bit-exact on integer inputs."""
+    assert mg.config_names()[mg.mi_sgemm_select_config(ta, tb, M, N, K)] == aligned_pick
     case = W.Case(f"unaligned_{layout}_{ta}{tb}_{M}x{N}x{K}", ta, tb, M, N, K, 1.0, -1.0, seed=61, fill="int_rand")
     note(case.name)
     inp = W.make_inputs(case)
