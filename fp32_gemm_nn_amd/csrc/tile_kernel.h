@@ -254,9 +254,9 @@ void sgemm_mfma32(GemmArgs g) {
     constexpr int A_FLOATS = ACopy::LDS_FLOATS, B_FLOATS = BCopy::LDS_FLOATS;
     constexpr int AS = ACopy::STRIDE, BS = BCopy::STRIDE;
     constexpr int GROUP_FLOATS = 2 * (A_FLOATS + B_FLOATS);
-    // The k-group reduction reuses the tile buffers: KG-1 groups x waves x
-    // FM*FN accumulator blocks x 16 registers x 64 lanes.
-    constexpr int RED_FLOATS = (KG - 1) * (NTG / 64) * FM * FN * AR * 64;
+    // The k-group reduction reuses the tile buffers: KG groups x waves x
+    // FM*FN accumulator blocks x AR registers x 64 lanes.
+    constexpr int RED_FLOATS = KG > 1 ? KG * (NTG / 64) * FM * FN * AR * 64 : 0;
     static_assert(RED_FLOATS <= KG * GROUP_FLOATS, "reduction does not fit the tile buffers");
 
     __shared__ __attribute__((aligned(16))) float lds[KG * GROUP_FLOATS];
@@ -274,9 +274,12 @@ void sgemm_mfma32(GemmArgs g) {
         // out of the tile loop and held live across every k-loop.
         int tid = threadIdx.x;
         if constexpr (CFG::STREAMK) asm volatile("" : "+v"(tid));
-        const int grp = KG == 1 ? 0 : tid / NTG;    // k-group
-        const int gtid = KG == 1 ? tid : tid % NTG;  // thread within it
-        const int lane = gtid & 63, wave = gtid >> 6;
+        // The k-group and the wave are the same for every lane of a wave:
+        // read from the first lane, they live in scalar registers, so the
+        // k-loop's trip count and the per-wave offsets are scalar too.
+        const int grp = KG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid / NTG);   // k-group
+        const int gtid = KG == 1 ? tid : tid % NTG;                                // thread within it
+        const int lane = gtid & 63, wave = __builtin_amdgcn_readfirstlane(gtid >> 6);
         // Lane column and group: (lane % 32, lane / 32) for 32 x 32 blocks,
         // (lane % 16, lane / 16) for 16 x 16 blocks.
         const int li = CFG::MI16 ? (lane & 15) : (lane & 31), lh = CFG::MI16 ? (lane >> 4) : (lane >> 5);
@@ -438,10 +441,42 @@ void sgemm_mfma32(GemmArgs g) {
             if (has_next) f0.template read<AS, BS>(lds, as_n, bs_n, 0, wm, wn, li, lh);
         }
 
-        if constexpr (KG > 1) {
-            // Groups 1..KG-1 hand their accumulators to group 0 through LDS (the
-            // tile buffers are free after the last barrier); group 0 adds them in
-            // group order, so the sum is the same on every call.
+        // k-groups without a split: every group writes its accumulators to LDS
+        // (the tile buffers are free after the last barrier), and group g then
+        // sums accumulator registers r = g, g + KG, ... of all KG groups, in
+        // group order (the same sum, in the same order, on every call), and
+        // stores those outputs; the reduction and the stores are shared by all
+        // the workgroup's waves.
+        static_assert(KG == 1 || AR % KG == 0, "k-groups split the accumulator registers evenly");
+        if constexpr (KG > 1 && !CFG::SPLIT) {
+            constexpr int WAVES = NTG / 64;
+            constexpr int BLOCKS = FM * FN;
+            // Register r of block b of wave w of group s at ((s*WAVES + w)*AR + r)*BLOCKS + b, times 64 lanes.
+            float *mine = lds + (grp * WAVES + wave) * AR * BLOCKS * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int r = 0; r < AR; ++r) mine[(r * BLOCKS + i * FN + j) * 64] = acc[i][j][r];
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < AR; ++r) {
+                if (r % KG != grp) continue;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const float *src = lds + wave * AR * BLOCKS * 64 + lane + (r * BLOCKS + i * FN + j) * 64;
+                        float sum = src[0];
+#pragma unroll
+                        for (int s2 = 1; s2 < KG; ++s2) sum += src[s2 * WAVES * AR * BLOCKS * 64];
+                        acc[i][j][r] = sum;
+                    }
+            }
+        } else if constexpr (KG > 1) {
+            // With a split, group 0 takes the partial block on: groups 1..KG-1
+            // hand their accumulators to it, and it adds them in group order.
             constexpr int SLOT = FM * FN * AR * 64;            // floats per wave
             constexpr int WAVES = NTG / 64;
             if (grp > 0) {
@@ -454,8 +489,6 @@ void sgemm_mfma32(GemmArgs g) {
                         for (int r = 0; r < AR; ++r) dst[((i * FN + j) * AR + r) * 64] = acc[i][j][r];
             }
             __syncthreads();
-            // Without split-K no barrier follows, so the other groups are done.
-            if (!CFG::SPLIT && grp > 0) return;
             if (grp == 0)
 #pragma unroll
             for (int g2 = 1; g2 < KG; ++g2) {
@@ -534,11 +567,12 @@ void sgemm_mfma32(GemmArgs g) {
             }
             if (tid == 0) __hip_atomic_store(&g.counters[tile_id], 0, __ATOMIC_RELAXED, kExchangeScope);
         }
-        if (grp > 0) return;
+        if (CFG::SPLIT && grp > 0) return;
 
         // Epilogue. Accumulator element r of block (i, j) in lane (li, lh) is
         // block row 8*(r/4) + 4*lh + r%4 (32 x 32 blocks) or 4*lh + r (16 x 16
-        // blocks), block column li.
+        // blocks), block column li. With k-groups and no split, group g stores
+        // the registers r = g (mod KG) it has summed.
         const float alpha = g.alpha, beta = g.beta;
         float *const cw = g.C + (size_t)(m0 + wm * WTM) * g.ldc + (n0 + wn * WTN);
         const int rows_left = M - (m0 + wm * WTM), cols_left = N - (n0 + wn * WTN);
@@ -547,6 +581,8 @@ void sgemm_mfma32(GemmArgs g) {
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int r = 0; r < AR; ++r) {
+                if constexpr (KG > 1 && !CFG::SPLIT)
+                    if (r % KG != grp) continue;
                 const int ib = CFG::MI16 ? 4 * lh + r : 8 * (r / 4) + 4 * lh + (r % 4);
                 const int row = TA ? FM * ib + i : MBLK * i + ib;
                 if (row >= rows_left) continue;
