@@ -611,10 +611,11 @@ void sgemm_mfma32(GemmArgs g) {
 
     if constexpr (CFG::STREAMK) {
         static_assert(KG == 1 && !CFG::SPLIT, "stream-K runs one k-group");
-        // The first sk_tiles tiles are shared out: iteration i is k-tile
-        // i % ktiles of tile i / ktiles (tiles in the grouped order), and
-        // workgroup w owns [start(w), start(w+1)); workgroups on one XCD own
-        // consecutive shares. The rest follow whole, one per workgroup per wave.
+        // The first sk_tiles tiles (fewer than the grid) are shared out:
+        // iteration i is k-tile i % ktiles of tile i / ktiles (tiles in the
+        // grouped order), and workgroup w owns [start(w), start(w+1));
+        // workgroups on one XCD own consecutive shares. The rest, whole waves of
+        // the grid, follow whole, one per workgroup per wave.
         // A tile cut between workgroups w0..w1 has one segment per workgroup.
         // Workgroup w keeps the partial of its first tile in slot 2w and of
         // its last in slot 2w+1; segment j > 0 of a tile always starts its
