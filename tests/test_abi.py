@@ -218,6 +218,20 @@ def test_shape_class_selection():
     # slots): two k-groups; exactly 512 keeps stream-K.
     assert sel("N", "N", 1844, 1056, 2032) == "mfma16_64x64x32_w2x2_kg2"
     assert sel("N", "T", 828, 2392, 3588) == "mfma16_64x64x32_w2x2_kg2"
+    # The edges of that band, with long K: 460 tiles of 64 x 64 (1280 x 1472)
+    # fill under 90% of two slots per CU and take stream-K (72..127 tiles of
+    # 128 x 128 with K >= 2048); 462 (1344 x 1408; 461 is prime, and no grid of
+    # 461 such tiles stays under 230 tiles of 128 x 128) and 511 (448 x 4672)
+    # take two k-groups; exactly 512 (1024 x 2048) keeps stream-K.
+    assert sel("N", "N", 1280, 1472, 4096) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "N", 1344, 1408, 4096) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 448, 4672, 4096) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 1024, 2048, 4096) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    # With short K (K < 1024) the short-k rule comes first: 512 tiles take the
+    # plain 64 x 64 tile, 460 and 462 still two k-groups.
+    assert sel("N", "N", 1024, 2048, 512) == "mfma16_64x64x32_w2x2"
+    assert sel("N", "N", 1344, 1408, 512) == "mfma16_64x64x32_w2x2_kg2"
+    assert sel("N", "N", 1280, 1472, 512) == "mfma16_64x64x32_w2x2_kg2"
     # ... and short k on up to 229 such tiles: the plain 64 x 64 tile.
     assert sel("N", "T", 1072, 2768, 764) == "mfma16_64x64x32_w2x2"
     assert sel("N", "N", 1536, 2048, 512) == "mfma16_64x64x32_w2x2"
