@@ -477,9 +477,10 @@ def run_table(path, steps, warmup):
             del prob
 
 
-def run_workload(name, steps, warmup, configs=None):
+def run_workload(name, steps, warmup, configs=None, preheat_s=0.0):
     """One workload with its chosen kernel, or with each of `configs` (names
-    or ids) forced: one JSON line of numbers per kernel."""
+    or ids) forced: one JSON line of numbers per kernel, each kernel preheated
+    for `preheat_s` seconds first."""
     import fp32_gemm_nn_amd as mg
     from synthetic import workloads as W
 
@@ -493,6 +494,8 @@ def run_workload(name, steps, warmup, configs=None):
     chosen = mg.mi_sgemm_select_config(case.transA, case.transB, case.M, case.N, case.K)
     ids = [None] if not configs else [int(c) if str(c).isdigit() else names.index(c) for c in configs]
     for cfg in ids:
+        if preheat_s > 0:
+            preheat(prob, preheat_s, config=cfg)
         _, ev = time_problem(prob, steps, warmup, config=cfg)
         per = ev / steps
         row = {"workload": case.name, "transA": case.transA, "transB": case.transB, "M": case.M, "N": case.N,
@@ -652,7 +655,8 @@ def main():
     ap.add_argument("--table", metavar="PATH", help="also write per-workload numbers to PATH")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--preheat", type=float, default=1.0,
-                    help="seconds of back-to-back calls before the warm-up steps (reported as `preheat`)")
+                    help="seconds of back-to-back calls before the warm-up steps (reported as `preheat`; "
+                         "with --workload, before each kernel's timing; 0 for none)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other workload families (the `configs` field)")
     ap.add_argument("--sweep-configs", metavar="PATH",
@@ -694,7 +698,7 @@ def main():
         run_copy(args.steps, args.warmup)
         return
     if args.workload:
-        run_workload(args.workload, args.steps, args.warmup, args.config)
+        run_workload(args.workload, args.steps, args.warmup, args.config, args.preheat)
         return
     if args.ladder:
         run_ladder(args.ladder)
