@@ -249,6 +249,47 @@ __device__ __forceinline__ void store_run(float *p, const float (&out)[n], float
         if (b < valid) p[b] = (beta != 0.0f) ? fmaf(beta, p[b], out[b]) : out[b];
 }
 
+// The n adjacent C values of one row that an epilogue batch will update: one
+// vector load when `whole`, else the first `valid` elements (the rest zero).
+template <int n>
+__device__ __forceinline__ void load_run(const float *p, float (&c)[n], bool whole, int valid) {
+    if constexpr (n == 2 || n == 4) {
+        if (whole) {
+            using V = typename VecOf<n>::type;
+            const V v = *reinterpret_cast<const V *>(p);
+#pragma unroll
+            for (int b = 0; b < n; ++b) c[b] = v[b];
+            return;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < n; ++b) c[b] = b < valid ? p[b] : 0.0f;
+}
+
+// C <- out + beta*c over n adjacent elements of one row, c being those
+// elements' values loaded beforehand (unused when beta == 0); one vector store
+// when `whole`, else the first `valid` elements.
+template <int n>
+__device__ __forceinline__ void put_run(float *p, const float (&out)[n], const float (&c)[n], float beta, bool whole,
+                                        int valid) {
+    float v[n];
+#pragma unroll
+    for (int b = 0; b < n; ++b) v[b] = beta != 0.0f ? fmaf(beta, c[b], out[b]) : out[b];
+    if constexpr (n == 2 || n == 4) {
+        if (whole) {
+            using V = typename VecOf<n>::type;
+            V w;
+#pragma unroll
+            for (int b = 0; b < n; ++b) w[b] = v[b];
+            *reinterpret_cast<V *>(p) = w;
+            return;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < n; ++b)
+        if (b < valid) p[b] = v[b];
+}
+
 // Launch index -> (tile row, tile column). Workgroup b runs on XCD b % 8; the
 // j-th workgroup of XCD x is given logical tile prefix(x) + j, so each XCD
 // walks one contiguous run of logical tiles. Logical tiles are ordered in

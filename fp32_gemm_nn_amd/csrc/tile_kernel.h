@@ -577,32 +577,116 @@ void sgemm_mfma32(GemmArgs g) {
         float *const cw = g.C + (size_t)(m0 + wm * WTM) * g.ldc + (n0 + wn * WTN);
         const int rows_left = M - (m0 + wm * WTM), cols_left = N - (n0 + wn * WTN);
         const int ldc = g.ldc;
+        // k-group tiles (a quarter or half of the row runs (i, r) per lane)
+        // and the 256 x 256 tiles (one tile per CU; batching measured no
+        // faster there) store run by run, reading C with each store where
+        // beta != 0.
+        constexpr bool RUN_BY_RUN = (KG > 1 && !CFG::SPLIT) || CFG::BM * CFG::BN >= 256 * 256;
+        if constexpr (RUN_BY_RUN) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+            for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int r = 0; r < AR; ++r) {
-                if constexpr (KG > 1 && !CFG::SPLIT)
-                    if (r % KG != grp) continue;
+                for (int r = 0; r < AR; ++r) {
+                    if constexpr (KG > 1 && !CFG::SPLIT)
+                        if (r % KG != grp) continue;
+                    const int ib = CFG::MI16 ? 4 * lh + r : 8 * (r / 4) + 4 * lh + (r % 4);
+                    const int row = TA ? FM * ib + i : MBLK * i + ib;
+                    if (row >= rows_left) continue;
+                    float *crow = cw + (size_t)row * ldc;
+                    if (!TB) {
+                        const int col = FN * li;
+                        float out[FN];
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) out[j] = alpha * acc[i][j][r];
+                        store_run<FN>(crow + col, out, beta, g.vec_c && col + FN <= cols_left, cols_left - col);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) {
+                            const int col = MBLK * j + li;
+                            if (col < cols_left) {
+                                float *p = crow + col;
+                                const float o = alpha * acc[i][j][r];
+                                *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
+                            }
+                        }
+                    }
+                }
+            }
+        } else {
+            // Row runs (i, r) are stored in turn when C is not read (beta ==
+            // 0). When it is, they go in batches of up to 32 values, and every
+            // C load of a batch is issued before the batch's first store, so
+            // the loads wait once, together. (Loaded and stored run by run,
+            // each load would wait for the store before it: nothing tells the
+            // compiler that the rows do not overlap.)
+            constexpr int RUNS = FM * AR;
+            constexpr int BATCH = 32 / FN < 1 ? 1 : (32 / FN > RUNS ? RUNS : 32 / FN);
+            // !TB: FN adjacent columns FN*li .. FN*li + FN-1; TB: columns MBLK*j + li.
+            const int col0 = FN * li;
+            const bool whole = g.vec_c && col0 + FN <= cols_left;
+            // Output row of run (i, r) within the wave's block, or -1 beyond M.
+            auto run_row = [&](int i, int r) {
                 const int ib = CFG::MI16 ? 4 * lh + r : 8 * (r / 4) + 4 * lh + (r % 4);
                 const int row = TA ? FM * ib + i : MBLK * i + ib;
-                if (row >= rows_left) continue;
+                return row < rows_left ? row : -1;
+            };
+            // Run (i, r) from acc and cin (C's values there; unused when beta == 0).
+            auto put = [&](int i, int r, int row, const float (&cin)[FN]) {
                 float *crow = cw + (size_t)row * ldc;
                 if (!TB) {
-                    // FN adjacent columns FN*li .. FN*li + FN-1.
-                    const int col = FN * li;
                     float out[FN];
 #pragma unroll
                     for (int j = 0; j < FN; ++j) out[j] = alpha * acc[i][j][r];
-                    store_run<FN>(crow + col, out, beta, g.vec_c && col + FN <= cols_left, cols_left - col);
+                    put_run<FN>(crow + col0, out, cin, beta, whole, cols_left - col0);
                 } else {
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
                         const int col = MBLK * j + li;
                         if (col < cols_left) {
-                            float *p = crow + col;
                             const float o = alpha * acc[i][j][r];
-                            *p = (beta != 0.0f) ? fmaf(beta, *p, o) : o;
+                            crow[col] = beta != 0.0f ? fmaf(beta, cin[j], o) : o;
                         }
+                    }
+                }
+            };
+            if (beta == 0.0f) {
+                float none[FN];
+#pragma unroll
+                for (int j = 0; j < FN; ++j) none[j] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int r = 0; r < AR; ++r) {
+                        const int row = run_row(i, r);
+                        if (row >= 0) put(i, r, row, none);
+                    }
+            } else {
+#pragma unroll
+                for (int b0 = 0; b0 < RUNS; b0 += BATCH) {
+                    float cin[BATCH][FN];
+#pragma unroll
+                    for (int u = 0; u < BATCH; ++u) {
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) cin[u][j] = 0.0f;
+                        if (b0 + u >= RUNS) continue;
+                        const int row = run_row((b0 + u) / AR, (b0 + u) % AR);
+                        if (row < 0) continue;
+                        const float *crow = cw + (size_t)row * ldc;
+                        if (!TB) {
+                            load_run<FN>(crow + col0, cin[u], whole, cols_left - col0);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < FN; ++j) {
+                                const int col = MBLK * j + li;
+                                if (col < cols_left) cin[u][j] = crow[col];
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < BATCH; ++u) {
+                        if (b0 + u >= RUNS) continue;
+                        const int row = run_row((b0 + u) / AR, (b0 + u) % AR);
+                        if (row >= 0) put((b0 + u) / AR, (b0 + u) % AR, row, cin[u]);
                     }
                 }
             }
