@@ -431,26 +431,36 @@ __global__ __launch_bounds__((64 * band_waves<MB, FAST>())) void sgemm_skinny_ba
         is_last = __hip_atomic_fetch_add(&sa.counters[tile], 1, __ATOMIC_RELAXED, kExchangeScope) == S - 1;
     __syncthreads();
     if (!is_last) return;
-    // The loads of eight splits are issued before they are summed; the sum
-    // runs in split order.
+    // The loads of eight splits, for all of this thread's outputs, are issued
+    // before any of them is summed or stored (a store to C ahead of the next
+    // output's loads would make those loads wait a round trip of their own);
+    // each output's sum runs in split order.
     const float *parts = sa.ws + (size_t)tile * S * T;
+    float sum[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) sum[i] = 0.0f;
+    for (int sp0 = 0; sp0 < S; sp0 += 8) {
+        float v[PER][8];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + NT * i;
+            const float *p = parts + (size_t)sp0 * T + idx;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[i][u] = (idx < T && sp0 + u < S)
+                              ? __hip_atomic_load(p + (size_t)u * T, __ATOMIC_RELAXED, kExchangeScope)
+                              : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (sp0 + u < S) sum[i] += v[i][u];
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int idx = tid + NT * i;
-        if (idx >= T) break;
-        float sum = 0.0f;
-        for (int sp0 = 0; sp0 < S; sp0 += 8) {
-            const float *p = parts + (size_t)sp0 * T + idx;
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = sp0 + i < S ? __hip_atomic_load(p + (size_t)i * T, __ATOMIC_RELAXED, kExchangeScope)
-                                   : 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (sp0 + i < S) sum += v[i];
-        }
-        finish(i, idx, sum);
+        if (idx < T) finish(i, idx, sum[i]);
     }
     if (tid == 0) __hip_atomic_store(&sa.counters[tile], 0, __ATOMIC_RELAXED, kExchangeScope);
 }
