@@ -39,7 +39,7 @@ size, used to calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters.
 from __future__ import annotations
 
 import argparse
-import hashlib
+import struct
 import json
 import os
 import sys
@@ -51,7 +51,6 @@ sys.path.insert(0, ROOT)
 METRIC = "SGEMM TFLOPS (2MNK/t) at 4096^3 and % of MI355X FP32 matrix peak"
 PEAK_FP32_MATRIX_TFLOPS = 157.3      # 256 CU x 2.4 GHz x 256 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0
-KERNEL_SRC_DIR = os.path.join(ROOT, "fp32_gemm_nn_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_nn_4096.json")
 COPY_BYTES = 256 << 20
 
@@ -64,26 +63,31 @@ def tflops(flops: float, seconds: float) -> float:
     return flops / seconds / 1e12
 
 
-def kernel_source_hash() -> str:
-    """sha256 over every HIP source and header of the library, by file name."""
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode() + b"\0")
-            with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
-                h.update(f.read())
-    return h.hexdigest()
+def kernel_code_hash(symbol):
+    """sha256 of one kernel's gfx950 machine code in the built library, or
+    None when the library or the kernel is missing."""
+    import fp32_gemm_nn_amd as mg
+    from fp32_gemm_nn_amd import codeobj
+
+    try:
+        return codeobj.kernel_code_sha256(mg.library_path, symbol)
+    except (OSError, KeyError, ValueError, struct.error):
+        return None
 
 
 def load_traffic(launch_flops_case):
     """HBM bytes per launch from the committed counter summary, or None if it
-    is missing or was taken on a different kernel source."""
+    is missing, is for another workload, or was taken on a kernel whose machine
+    code differs from the built one (the counters measure that code alone)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_hash() or t.get("workload") != launch_flops_case:
+    if t.get("workload") != launch_flops_case or not t.get("kernel_symbol"):
+        return None
+    code = kernel_code_hash(t["kernel_symbol"])
+    if code is None or t.get("kernel_code_sha256") != code:
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -1,13 +1,16 @@
 """Host-side logic of bench.py, on the CPU: the one-GPU guard, the kernel
-source hash, and the rule that the counter-derived traffic figure is reported
-only while it was taken on the current kernel sources."""
+code hash, and the rule that the counter-derived traffic figure is reported
+only while the built kernel's machine code is the code it was taken on."""
+import hashlib
 import json
 import os
-import shutil
 import subprocess
 import sys
 
+import pytest
+
 import bench
+import fp32_gemm_nn_amd as mg
 from synthetic import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -27,36 +30,37 @@ def test_world_size_above_one_is_refused():
     assert r.returncode == 2
 
 
-def _copy_sources(tmp_path):
-    d = tmp_path / "csrc"
-    shutil.copytree(bench.KERNEL_SRC_DIR, d)
-    return d
+HEADLINE_KERNEL = r"sgemm_mfma32INS_7TileCfgILi256ELi256ELi32ELi4ELi2ELi1ELi0ELb0ELb0ELb0ELb0EEELb0ELb0ELb0E"
 
 
-def test_source_hash_covers_every_source_and_header(tmp_path, monkeypatch):
-    d = _copy_sources(tmp_path)
-    monkeypatch.setattr(bench, "KERNEL_SRC_DIR", str(d))
-    h0 = bench.kernel_source_hash()
-    assert h0 == bench.kernel_source_hash()
-    names = sorted(n for n in os.listdir(d) if n.endswith((".hip", ".h")))
-    assert len(names) >= 4
-    for name in names:
-        p = d / name
-        text = p.read_bytes()
-        p.write_bytes(text + b"\n")
-        assert bench.kernel_source_hash() != h0, f"{name} is not covered by the hash"
-        p.write_bytes(text)
-    assert bench.kernel_source_hash() == h0
-    # Files that are not sources do not count.
-    (d / "notes.txt").write_text("x")
-    assert bench.kernel_source_hash() == h0
-    # A renamed file changes the hash even with the same bytes.
-    os.rename(d / names[0], d / ("z" + names[0]))
-    assert bench.kernel_source_hash() != h0
+def _built():
+    if not os.path.exists(mg.library_path):
+        pytest.skip("library not built")
+
+
+def test_kernel_code_hash_is_the_kernels_machine_code():
+    """The traffic record is tied to one kernel's gfx950 machine code, read from
+    the built library's code objects."""
+    _built()
+    from fp32_gemm_nn_amd import codeobj
+
+    code = codeobj.kernel_code(mg.library_path)
+    assert len(code) > 200
+    sym = codeobj.find_symbol(mg.library_path, HEADLINE_KERNEL)
+    h = bench.kernel_code_hash(sym)
+    assert h == hashlib.sha256(code[sym]).hexdigest()
+    # Whole instructions, and a different kernel hashes differently.
+    assert len(code[sym]) % 4 == 0 and len(code[sym]) > 4096
+    other = next(n for n in code if n != sym and "sgemm_mfma32" in n)
+    assert bench.kernel_code_hash(other) != h
+    assert bench.kernel_code_hash("_Z_no_such_kernel") is None
 
 
 def _traffic_file(tmp_path, **fields):
-    t = {"workload": W.HEADLINE.name, "kernel_source_sha256": bench.kernel_source_hash(),
+    from fp32_gemm_nn_amd import codeobj
+
+    sym = codeobj.find_symbol(mg.library_path, HEADLINE_KERNEL)
+    t = {"workload": W.HEADLINE.name, "kernel_symbol": sym, "kernel_code_sha256": bench.kernel_code_hash(sym),
          "hbm_bytes_per_launch": 123456789}
     t.update(fields)
     p = tmp_path / "traffic.json"
@@ -64,13 +68,19 @@ def _traffic_file(tmp_path, **fields):
     return p
 
 
-def test_traffic_reported_when_taken_on_these_sources(tmp_path, monkeypatch):
+def test_traffic_reported_when_taken_on_this_kernel_code(tmp_path, monkeypatch):
+    _built()
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(_traffic_file(tmp_path)))
     assert bench.load_traffic(W.HEADLINE.name) == 123456789
 
 
-def test_traffic_null_on_other_sources_workload_or_bad_file(tmp_path, monkeypatch):
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(_traffic_file(tmp_path, kernel_source_sha256="0" * 64)))
+def test_traffic_null_on_other_code_workload_or_bad_file(tmp_path, monkeypatch):
+    _built()
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(_traffic_file(tmp_path, kernel_code_sha256="0" * 64)))
+    assert bench.load_traffic(W.HEADLINE.name) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(_traffic_file(tmp_path, kernel_symbol="_Z_no_such_kernel")))
+    assert bench.load_traffic(W.HEADLINE.name) is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(_traffic_file(tmp_path, kernel_symbol=None)))
     assert bench.load_traffic(W.HEADLINE.name) is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(_traffic_file(tmp_path)))
     assert bench.load_traffic("nn_1024") is None
