@@ -40,7 +40,8 @@
 //     instantiation for unaligned operands), whose extra values only reach
 //     outputs beyond M or N. Stores are masked to i < M, j < N.
 //   * Epilogue: C = alpha*acc + beta*C fused into the store (itan.pw page,
-//     sections 3.4-3.5); when beta == 0, C is not read.
+//     sections 3.4-3.5); when beta == 0, C is not read, else a batch of C
+//     values is loaded before any of them is stored.
 //   * Workgroup order: consecutive workgroups are dealt round-robin to the 8
 //     XCDs, each with its own L2. The launch index is remapped so each XCD
 //     receives one contiguous run of tiles, walked in column groups of
