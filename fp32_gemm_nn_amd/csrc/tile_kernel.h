@@ -582,6 +582,10 @@ void sgemm_mfma32(GemmArgs g) {
         // faster there) store run by run, reading C with each store where
         // beta != 0.
         constexpr bool RUN_BY_RUN = (KG > 1 && !CFG::SPLIT) || CFG::BM * CFG::BN >= 256 * 256;
+        // Staged through LDS (B transposed): every wave's block, unpadded,
+        // within the tile buffers.
+        constexpr bool STAGE_C = TB && !RUN_BY_RUN && KG == 1 && (NTG / 64) * WTM * WTN <= GROUP_FLOATS &&
+                                 (WTM * WTN) % 256 == 0 && WTN % 32 == 0;
         if constexpr (RUN_BY_RUN) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -613,80 +617,138 @@ void sgemm_mfma32(GemmArgs g) {
                 }
             }
         } else {
-            // Row runs (i, r) are stored in turn when C is not read (beta ==
-            // 0). When it is, they go in batches of up to 32 values, and every
-            // C load of a batch is issued before the batch's first store, so
-            // the loads wait once, together. (Loaded and stored run by run,
-            // each load would wait for the store before it: nothing tells the
-            // compiler that the rows do not overlap.)
-            constexpr int RUNS = FM * AR;
-            constexpr int BATCH = 32 / FN < 1 ? 1 : (32 / FN > RUNS ? RUNS : 32 / FN);
-            // !TB: FN adjacent columns FN*li .. FN*li + FN-1; TB: columns MBLK*j + li.
-            const int col0 = FN * li;
-            const bool whole = g.vec_c && col0 + FN <= cols_left;
-            // Output row of run (i, r) within the wave's block, or -1 beyond M.
-            auto run_row = [&](int i, int r) {
-                const int ib = CFG::MI16 ? 4 * lh + r : 8 * (r / 4) + 4 * lh + (r % 4);
-                const int row = TA ? FM * ib + i : MBLK * i + ib;
-                return row < rows_left ? row : -1;
-            };
-            // Run (i, r) from acc and cin (C's values there; unused when beta == 0).
-            auto put = [&](int i, int r, int row, const float (&cin)[FN]) {
-                float *crow = cw + (size_t)row * ldc;
-                if (!TB) {
-                    float out[FN];
+            // B transposed and C read (beta != 0): a lane's FN outputs of a row
+            // sit MBLK columns apart and would be loaded and stored as 4-byte
+            // accesses. Each wave writes its block to its own part of the tile
+            // buffers (free once the k-loop has ended on a barrier), reads it
+            // back as rows of 16-byte runs, loads all of its C runs, and stores
+            // the runs, 256 contiguous bytes per 16 lanes. (With beta == 0 the
+            // staging costs more than the 4-byte stores: 2048^3 NT 132.7 vs
+            // 130.4 us.)
+            bool staged = false;
+            if constexpr (STAGE_C) {
+                if (beta != 0.0f) {
+                    constexpr int RUNS4 = WTM * WTN / 256;    // 16-byte runs per lane
+                    // The 16-float halves of each 32-column group swap places on
+                    // rows whose bit SH is set: the four rows one write instruction
+                    // covers (4*lh apart, or 4*FM*lh with A transposed) then fall on
+                    // both halves of the banks, and a 16-byte run never straddles a
+                    // half.
+                    constexpr int SH = TA ? (FM == 1 ? 2 : (FM == 2 ? 3 : 4)) : 2;
+                    auto sidx = [&](int row, int col) { return row * WTN + (col ^ (((row >> SH) & 1) << 4)); };
+                    float *st = lds + wave * WTM * WTN;
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) out[j] = alpha * acc[i][j][r];
-                    put_run<FN>(crow + col0, out, cin, beta, whole, cols_left - col0);
-                } else {
+                    for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        const int col = MBLK * j + li;
-                        if (col < cols_left) {
-                            const float o = alpha * acc[i][j][r];
-                            crow[col] = beta != 0.0f ? fmaf(beta, cin[j], o) : o;
+                        for (int r = 0; r < AR; ++r) {
+                            const int ib = CFG::MI16 ? 4 * lh + r : 8 * (r / 4) + 4 * lh + (r % 4);
+                            const int row = TA ? FM * ib + i : MBLK * i + ib;
+#pragma unroll
+                            for (int j = 0; j < FN; ++j) st[sidx(row, MBLK * j + li)] = acc[i][j][r];
                         }
+                    __syncthreads();
+                    float out[RUNS4][4], cin[RUNS4][4];
+#pragma unroll
+                    for (int u = 0; u < RUNS4; ++u) {
+                        const int flat = (u * 64 + lane) * 4, row = flat / WTN, col = flat % WTN;
+                        LdsVec<4>::get(st + sidx(row, col), out[u]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            out[u][e] *= alpha;
+                            cin[u][e] = 0.0f;
+                        }
+                        if (row < rows_left)
+                            load_run<4>(cw + (size_t)row * ldc + col, cin[u], g.vec_c && col + 4 <= cols_left,
+                                        cols_left - col);
                     }
+#pragma unroll
+                    for (int u = 0; u < RUNS4; ++u) {
+                        const int flat = (u * 64 + lane) * 4, row = flat / WTN, col = flat % WTN;
+                        if (row < rows_left)
+                            put_run<4>(cw + (size_t)row * ldc + col, out[u], cin[u], beta,
+                                       g.vec_c && col + 4 <= cols_left, cols_left - col);
+                    }
+                    // A stream-K workgroup's next tile writes the tile buffers next.
+                    if constexpr (CFG::STREAMK) __syncthreads();
+                    staged = true;
                 }
-            };
-            if (beta == 0.0f) {
-                float none[FN];
+            }
+            if (!staged) {
+                // Row runs (i, r) are stored in turn when C is not read (beta ==
+                // 0). When it is, they go in batches of up to 32 values, and every
+                // C load of a batch is issued before the batch's first store, so
+                // the loads wait once, together. (Loaded and stored run by run,
+                // each load would wait for the store before it: nothing tells the
+                // compiler that the rows do not overlap.)
+                constexpr int RUNS = FM * AR;
+                constexpr int BATCH = 32 / FN < 1 ? 1 : (32 / FN > RUNS ? RUNS : 32 / FN);
+                // !TB: FN adjacent columns FN*li .. FN*li + FN-1; TB: columns MBLK*j + li.
+                const int col0 = FN * li;
+                const bool whole = g.vec_c && col0 + FN <= cols_left;
+                // Output row of run (i, r) within the wave's block, or -1 beyond M.
+                auto run_row = [&](int i, int r) {
+                    const int ib = CFG::MI16 ? 4 * lh + r : 8 * (r / 4) + 4 * lh + (r % 4);
+                    const int row = TA ? FM * ib + i : MBLK * i + ib;
+                    return row < rows_left ? row : -1;
+                };
+                // Run (i, r) from acc and cin (C's values there; unused when beta == 0).
+                auto put = [&](int i, int r, int row, const float (&cin)[FN]) {
+                    float *crow = cw + (size_t)row * ldc;
+                    if (!TB) {
+                        float out[FN];
 #pragma unroll
-                for (int j = 0; j < FN; ++j) none[j] = 0.0f;
+                        for (int j = 0; j < FN; ++j) out[j] = alpha * acc[i][j][r];
+                        put_run<FN>(crow + col0, out, cin, beta, whole, cols_left - col0);
+                    } else {
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int r = 0; r < AR; ++r) {
-                        const int row = run_row(i, r);
-                        if (row >= 0) put(i, r, row, none);
-                    }
-            } else {
-#pragma unroll
-                for (int b0 = 0; b0 < RUNS; b0 += BATCH) {
-                    float cin[BATCH][FN];
-#pragma unroll
-                    for (int u = 0; u < BATCH; ++u) {
-#pragma unroll
-                        for (int j = 0; j < FN; ++j) cin[u][j] = 0.0f;
-                        if (b0 + u >= RUNS) continue;
-                        const int row = run_row((b0 + u) / AR, (b0 + u) % AR);
-                        if (row < 0) continue;
-                        const float *crow = cw + (size_t)row * ldc;
-                        if (!TB) {
-                            load_run<FN>(crow + col0, cin[u], whole, cols_left - col0);
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < FN; ++j) {
-                                const int col = MBLK * j + li;
-                                if (col < cols_left) cin[u][j] = crow[col];
+                        for (int j = 0; j < FN; ++j) {
+                            const int col = MBLK * j + li;
+                            if (col < cols_left) {
+                                const float o = alpha * acc[i][j][r];
+                                crow[col] = beta != 0.0f ? fmaf(beta, cin[j], o) : o;
                             }
                         }
                     }
+                };
+                if (beta == 0.0f) {
+                    float none[FN];
 #pragma unroll
-                    for (int u = 0; u < BATCH; ++u) {
-                        if (b0 + u >= RUNS) continue;
-                        const int row = run_row((b0 + u) / AR, (b0 + u) % AR);
-                        if (row >= 0) put((b0 + u) / AR, (b0 + u) % AR, row, cin[u]);
+                    for (int j = 0; j < FN; ++j) none[j] = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int r = 0; r < AR; ++r) {
+                            const int row = run_row(i, r);
+                            if (row >= 0) put(i, r, row, none);
+                        }
+                } else {
+#pragma unroll
+                    for (int b0 = 0; b0 < RUNS; b0 += BATCH) {
+                        float cin[BATCH][FN];
+#pragma unroll
+                        for (int u = 0; u < BATCH; ++u) {
+#pragma unroll
+                            for (int j = 0; j < FN; ++j) cin[u][j] = 0.0f;
+                            if (b0 + u >= RUNS) continue;
+                            const int row = run_row((b0 + u) / AR, (b0 + u) % AR);
+                            if (row < 0) continue;
+                            const float *crow = cw + (size_t)row * ldc;
+                            if (!TB) {
+                                load_run<FN>(crow + col0, cin[u], whole, cols_left - col0);
+                            } else {
+#pragma unroll
+                                for (int j = 0; j < FN; ++j) {
+                                    const int col = MBLK * j + li;
+                                    if (col < cols_left) cin[u][j] = crow[col];
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int u = 0; u < BATCH; ++u) {
+                            if (b0 + u >= RUNS) continue;
+                            const int row = run_row((b0 + u) / AR, (b0 + u) % AR);
+                            if (row >= 0) put((b0 + u) / AR, (b0 + u) % AR, row, cin[u]);
+                        }
                     }
                 }
             }
