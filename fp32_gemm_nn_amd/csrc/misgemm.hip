@@ -363,8 +363,11 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const bool big_ok = !(K < 2048 && t128 < 4 * kNumCus);
         const bool tt = ta && tb;
         const bool wide = !tt && M < N;    // 128 x 256 rather than 256 x 128
-        // With both transposed, the 256 x 256 tile with direct-to-LDS loads
-        // (the register-staged one spills): 960 vs 989 us for 256 x 128 at 4096^3.
+        // With A transposed, the 256 x 256 tile with direct-to-LDS loads: for
+        // TT the register-staged one spills (960 vs 989 us for 256 x 128 at
+        // 4096^3); for TN it is 0.6-1.7% faster than the register-staged one
+        // (4096^3 947 vs 960 us, 8192 x 8192 x 2048 1904 vs 1929, 4000^3 1028
+        // vs 1035).
         // Its edge tiles run the guarded k-loop (the smaller tiles clamp their
         // edge loads instead), so a 256 x 256 grid that does not divide M and N
         // scores lower (4000^3: 1022 us against 951 for 128 x 256 x 16).
@@ -391,7 +394,7 @@ int select_config(char transA, char transB, int M, int N, int K) {
         const double s_sk16 = (sk_ok && (!tb || (ta && kt >= 64))) ? 0.965 : -1.0;
         const double best =
             fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(fmax(s_128, s_64), s_sk16));
-        if (best == s_q) return tt ? kCfg256x256Dl : kCfg256x256;
+        if (best == s_q) return ta ? kCfg256x256Dl : kCfg256x256;
         if (best == s_sk16) return kCfg16StreamK1;
         if (best == s_skb) return wide ? kCfgStreamK128x256 : kCfgStreamK256x128;
         if (best == s_sk) return kCfgStreamK2;

@@ -109,7 +109,8 @@ def test_with_config_rejects_unknown_id():
 def test_selection_fuzz():
     """Seeded random shapes: the pick is always a valid matrix-core
     configuration (never a vector-ALU ladder rung), the band kernel exactly
-    when M <= 32 and N >= 128, and the direct-to-LDS 256 x 256 tile only for TT."""
+    when M <= 32 and N >= 128, and the direct-to-LDS 256 x 256 tile only with
+    A transposed."""
     import random
 
     names = mg.config_names()
@@ -125,10 +126,10 @@ def test_selection_fuzz():
         assert not name.startswith("valu_"), (ta, tb, M, N, K, name)
         assert ("band" in name) == (M <= 32 and N >= 128), (ta, tb, M, N, K, name)
         if name.endswith("_dl"):
-            assert ta in "TtCc" and tb in "TtCc" and name == "mfma32_256x256x32_w4x2_dl", (ta, tb, M, N, K, name)
-        # The register-staged 256 x 256 tile spills with both operands
-        # transposed; TT takes its direct-to-LDS form.
-        if ta in "TtCc" and tb in "TtCc":
+            assert ta in "TtCc" and name == "mfma32_256x256x32_w4x2_dl", (ta, tb, M, N, K, name)
+        # With A transposed the 256 x 256 tile takes its direct-to-LDS form
+        # (the register-staged one spills for TT and is slower for TN).
+        if ta in "TtCc":
             assert name != "mfma32_256x256x32_w4x2", (ta, tb, M, N, K, name)
 
 
@@ -137,9 +138,10 @@ def test_shape_class_selection():
     sel = lambda *s: names[mg.mi_sgemm_select_config(*s)]
     # 4096^2 output: 256 tiles of 256 x 256, one per CU.
     assert sel("N", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
-    assert sel("T", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
     assert sel("N", "T", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2"
-    # Both transposed: the 256 x 256 tile with direct-to-LDS loads.
+    # A transposed: the 256 x 256 tile with direct-to-LDS loads.
+    assert sel("T", "N", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2_dl"
+    assert sel("T", "N", 8192, 8192, 2048) == "mfma32_256x256x32_w4x2_dl"
     assert sel("T", "T", 4096, 4096, 4096) == "mfma32_256x256x32_w4x2_dl"
     assert sel("T", "T", 4096, 4096, 1024) == "mfma32_256x256x32_w4x2_dl"
     assert sel("T", "T", 2048, 4096, 2048) == "mfma32_256x128x32_w4x2"

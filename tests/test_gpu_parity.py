@@ -139,6 +139,9 @@ INT_CASES = [
     W.C5B.with_(name="int_skinny", fill="int_rand"),
     *[c.with_(name="int_" + c.name, fill="int_rand", alpha=2.0, beta=-1.0) for c in W.C5A],
     *[W.c3(n).with_(name=f"int_sweep_{n}", fill="int_rand", alpha=0.5, beta=-2.0) for n in (256, 768, 1280, 2304)],
+    # The 256 x 256 tiles for the transposed op pairs (direct-to-LDS for TN and TT).
+    *[W.Case(f"int_{ta}{tb}_4096x4096x512".lower(), ta, tb, 4096, 4096, 512, 1.0, -1.0, seed=77, fill="int_rand")
+      for ta, tb in (("N", "T"), ("T", "N"), ("T", "T"))],
 ]
 
 

@@ -9,11 +9,10 @@ section „Çà„Åè„ÅÇ„ÇãËêΩ„Å®„ÅóÁ©¥„Å®„ÉÅ„Çß„ÉÉ„ÇØ„É™„Çπ„Éà, item 4, ÈÅéÂ∫¶„Å™„É¨„Ç
 registers go to slow local memory).
 
 No instantiation the shape-class selection can reach may spill, for any op
-pair, aligned or not. Two forced-only instantiations are allowed to: the
-register-staged 256 x 256 tile with both operands transposed (TT takes the
-direct-to-LDS form) and the direct-to-LDS 256 x 256 tile with only A
-transposed (direct-to-LDS is chosen only for TT); test_abi's selection fuzz
-checks that neither is ever chosen.
+pair, aligned or not. One forced-only instantiation is allowed to: the
+register-staged 256 x 256 tile with both operands transposed (with A
+transposed the selection takes the direct-to-LDS form); test_abi's selection
+fuzz checks that it is never chosen.
 """
 import os
 
@@ -24,13 +23,10 @@ from fp32_gemm_nn_amd import codeobj
 
 msgpack = pytest.importorskip("msgpack")
 
-# Mangled-name fragments of the two forced-only instantiations that spill:
-# TileCfg<256,256,32,4,2,1,0,false,false,false,false> with TA = TB = true, and
-# TileCfg<256,256,32,4,2,1,0,false,false,true,false> (direct-to-LDS) with
-# TA = true, TB = false.
+# Mangled-name fragment of the forced-only instantiation that spills:
+# TileCfg<256,256,32,4,2,1,0,false,false,false,false> with TA = TB = true.
 FORCED_ONLY_SPILLING = {
     "TileCfgILi256ELi256ELi32ELi4ELi2ELi1ELi0ELb0ELb0ELb0ELb0EEELb1ELb1ELb0E": "256x256 register-staged, TT",
-    "TileCfgILi256ELi256ELi32ELi4ELi2ELi1ELi0ELb0ELb0ELb1ELb0EEELb1ELb0ELb0E": "256x256 direct-to-LDS, TN",
 }
 
 
@@ -60,8 +56,8 @@ def test_no_selectable_kernel_spills(kernels):
 
 
 def test_no_selectable_kernel_spills_vgprs(kernels):
-    """The metadata's own spill count agrees: no VGPR spilled outside the two
-    forced-only instantiations."""
+    """The metadata's own spill count agrees: no VGPR spilled outside the
+    forced-only instantiation."""
     spilling = {k[".name"]: k.get(".vgpr_spill_count", 0) for k in kernels if k.get(".vgpr_spill_count", 0)}
     unexpected = {n: s for n, s in spilling.items() if not any(frag in n for frag in FORCED_ONLY_SPILLING)}
     assert not unexpected, f"kernels with spilled VGPRs: {unexpected}"
