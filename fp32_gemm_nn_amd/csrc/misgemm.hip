@@ -124,6 +124,7 @@ using Cfg16L = TileCfg<128, 128, 32, 2, 2, 1, 0, false, false, false, true>;
 using Cfg16W = TileCfg<256, 128, 32, 4, 2, 1, 0, false, false, false, true>;
 using Cfg16L42D = TileCfg<128, 128, 32, 4, 2, 1, 4, false, false, true, true>;
 using Cfg16S4D = TileCfg<64, 64, 32, 2, 2, 4, 0, false, false, true, true>;
+using Cfg16Q12 = TileCfg<192, 192, 32, 4, 3, 1, 0, false, false, false, true>;   // 12 waves, 48 x 64 per wave
 
 // Config ids: the index of each entry of kConfigs below.
 enum ConfigId : int {
@@ -162,6 +163,7 @@ enum ConfigId : int {
     kCfg16x256x128 = 34,
     kCfg16x128W42Dl = 35,
     kCfg16x64Kg4Dl = 36,
+    kCfg16x192W43 = 37,
 };
 
 struct ConfigInfo {
@@ -207,10 +209,11 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma16_256x128x32_w4x2", Cfg16W::BM, Cfg16W::BN, Cfg16W::NT},
     {"mfma16_128x128x32_w4x2_dl", Cfg16L42D::BM, Cfg16L42D::BN, Cfg16L42D::NT},
     {"mfma16_64x64x32_w2x2_kg4_dl", Cfg16S4D::BM, Cfg16S4D::BN, Cfg16S4D::NT},
+    {"mfma16_192x192x32_w4x3", Cfg16Q12::BM, Cfg16Q12::BN, Cfg16Q12::NT},
 };
 constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-static_assert(kNumConfigs == kCfg16x64Kg4Dl + 1, "one ConfigId per kConfigs entry");
+static_assert(kNumConfigs == kCfg16x192W43 + 1, "one ConfigId per kConfigs entry");
 static_assert(kCfgLadderLast + 1 == kCfg256x256Dl, "the ladder ids are contiguous");
 static_assert(kConfigs[kCfg128].bm == CfgL::BM && kConfigs[kCfg128].bn == CfgL::BN && kConfigs[kCfg128].nt == CfgL::NT, "kConfigs order");
 static_assert(kConfigs[kCfg64].bm == CfgS::BM && kConfigs[kCfg64].bn == CfgS::BN && kConfigs[kCfg64].nt == CfgS::NT, "kConfigs order");
@@ -406,9 +409,18 @@ int select_config(char transA, char transB, int M, int N, int K) {
         // 75%) and for TT from K = 2048 (1792 x 3584 x 2048: 80% vs 76%), while
         // NT keeps the big-tile stream-K (1792 x 3584 x 4096: 85% vs 83%).
         const double s_sk16 = (sk_ok && (!tb || (ta && kt >= 64))) ? 0.965 * filled(128, 128) : -1.0;
-        const double best =
-            fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)), fmax(fmax(s_128, s_64), s_sk16));
+        // The 192 x 192 tile (twelve waves, one workgroup per CU), on grids
+        // that fill at least 88% of its waves, also at short K: 3072^3 410 us
+        // against 427 for stream-K, 6144^3 3231 against 3273 for 128 x 128,
+        // 3072 x 3072 x 512 76.2 against 81.8 for 64 x 64, 3000^3 403 against
+        // 427. Weight fitted on 84 seeded shapes near the boundary (mean regret
+        // 1.28% -> 0.63%); on 200-220 tiles it loses to 128 x 128 by ~9%.
+        const double b_192 = cu_balance(tiles(192, 192));
+        const double s_192 = b_192 >= 0.88 ? 1.03 * b_192 * filled(192, 192) : -1.0;
+        const double best = fmax(fmax(fmax(s_q, fmax(s_skb, s_sk)), fmax(s_b4, s_b8)),
+                                 fmax(fmax(fmax(s_128, s_64), s_sk16), s_192));
         if (best == s_q) return ta ? kCfg256x256Dl : kCfg256x256;
+        if (best == s_192) return kCfg16x192W43;
         if (best == s_sk16) return kCfg16StreamK1;
         if (best == s_skb) return wide ? kCfgStreamK128x256 : kCfgStreamK256x128;
         if (best == s_sk) return kCfgStreamK2;
@@ -475,6 +487,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 template <class CFG, bool TA, bool TB>
 constexpr bool kScalarForm =
     kClampEdge<CFG> && !std::is_same_v<CFG, CfgT16> && !std::is_same_v<CFG, CfgL42S2> &&
+    !std::is_same_v<CFG, Cfg16Q12> &&
     !(std::is_same_v<CFG, Cfg16L42> && !(!TA && TB)) &&
     !((std::is_same_v<CFG, CfgL24> || std::is_same_v<CFG, CfgL42>) && TA && !TB);
 
@@ -498,7 +511,8 @@ int unaligned_substitute(int config, bool ta, bool tb, int M, int N) {
         case kCfg256x256:
         case kCfg256x256Dl: return (ta && tb) ? kCfg128x256 : kCfg256x128;
         case kCfg128x256x16: return wide && !(ta && tb) ? kCfg128x256 : kCfg256x128;
-        case kCfgStreamK2: return kCfg16StreamK1;
+        case kCfgStreamK2:
+        case kCfg16x192W43: return kCfg16StreamK1;
         case kCfg16x128W42:
             if (!ta && tb) return config;
             return (tiles(256, 128) >= kNumCus && cu_balance(tiles(256, 128)) >= 0.9) ? kCfg256x128
@@ -923,6 +937,7 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case kCfg16x256x128: err = launch_cfg<Cfg16W>(ta, tb, g, stream, wsrc); break;
         case kCfg16x128W42Dl: err = launch_cfg<Cfg16L42D>(ta, tb, g, stream, wsrc); break;
         case kCfg16x64Kg4Dl: err = launch_cfg<Cfg16S4D>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x192W43: err = launch_cfg<Cfg16Q12>(ta, tb, g, stream, wsrc); break;
         default: err = launch_cfg<CfgTS>(ta, tb, g, stream, wsrc); break;   // kCfgStreamK128x256
     }
     if (wsrc.overflow) return MISGEMM_SCRATCH_TOO_SMALL;

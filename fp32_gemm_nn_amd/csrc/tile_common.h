@@ -97,6 +97,9 @@ template <> struct LdsVec<2> {
         out[0] = v[0]; out[1] = v[1];
     }
 };
+template <> struct LdsVec<3> {
+    static __device__ __forceinline__ void get(const float *p, float *out) { out[0] = p[0]; out[1] = p[1]; out[2] = p[2]; }
+};
 template <> struct LdsVec<4> {
     static __device__ __forceinline__ void get(const float *p, float *out) {
         f32x4 v = *reinterpret_cast<const f32x4 *>(p);

@@ -94,8 +94,8 @@ struct Frag {
 template <class CFG, bool TA, bool TB>
 struct Frag16 {
     static constexpr int FM = CFG::FM, FN = CFG::FN, WTM = CFG::WTM, WTN = CFG::WTN;
-    static_assert(!TA || FM == 1 || FM == 2 || FM == 4, "one LDS read covers a row's FM blocks");
-    static_assert(TB || FN == 1 || FN == 2 || FN == 4, "one LDS read covers a row's FN blocks");
+    static_assert(!TA || (FM >= 1 && FM <= 4), "one LDS read covers a row's FM blocks");
+    static_assert(TB || (FN >= 1 && FN <= 4), "one LDS read covers a row's FN blocks");
     float a[FM][4];
     float b[FN][4];
 
@@ -226,11 +226,12 @@ __device__ __forceinline__ void schedule_iteration() {
     }
 }
 
-// Register-staged tiles up to 256 x 128 fetch every complete k-tile with
-// clamped loads, so edge tiles keep the straight-line rounds (the 256 x 256
-// tile has no registers to spare for the clamped offsets).
+// Register-staged tiles up to 256 x 128, and the 192 x 192 tile, fetch every
+// complete k-tile with clamped loads, so edge tiles keep the straight-line
+// rounds (the 256 x 256 tile has no registers to spare for the clamped
+// offsets).
 template <class CFG>
-constexpr bool kClampEdge = !CFG::DL && CFG::BM * CFG::BN <= 256 * 128;
+constexpr bool kClampEdge = !CFG::DL && CFG::BM * CFG::BN <= 192 * 192;
 
 // SCALAR: the instantiation launched when A or B cannot be read with 16-byte
 // loads (pointer or leading dimension not a multiple of 4 floats); its

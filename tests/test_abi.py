@@ -193,14 +193,25 @@ def test_shape_class_selection():
     # Stream-K over 256 x 128 tiles where no data-parallel tile spreads evenly.
     skw = "mfma32_256x128x32_w4x2_streamk"
     sk16 = "mfma16_128x128x32_w4x2_streamk_1wg"
+    q192 = "mfma16_192x192x32_w4x3"
     for n, want in [(2048, "mfma16_128x128x32_w4x2"), (2304, sk16), (2560, sk16), (2816, "mfma32_256x128x32_w4x2"),
-                    (3072, sk16), (3328, sk16), (3584, sk16), (3840, sk16), (4096, "mfma32_256x256x32_w4x2"),
-                    (8192, "mfma32_256x256x32_w4x2")]:
+                    (3072, q192), (3328, sk16), (3584, sk16), (3840, sk16), (4096, "mfma32_256x256x32_w4x2"),
+                    (6144, q192), (8192, "mfma32_256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == want, n
+    # The 192 x 192 tile where its grid fills at least 88% of a whole number of
+    # waves (3072^2: 256 tiles; 3000 x 2900: 256, 92% of them outputs), every op
+    # pair, also at short K; not on 209 tiles (82%), nor on 484 (4096^2).
+    for ta in "NT":
+        for tb in "NT":
+            assert sel(ta, tb, 3072, 3072, 3072) == q192
+            assert sel(ta, tb, 3000, 2900, 700) == q192
+    assert sel("N", "N", 3072, 3072, 512) == q192
+    assert sel("N", "N", 1536, 6144, 4096) == q192
+    assert sel("T", "T", 2112, 3636, 3684) == sk16
     # Stream-K over big tiles for NT; over 128 x 128 tiles of 16 x 16 blocks for
     # TN, and for TT from K = 2048; 128 x 128 (two per CU) where big tiles do not pay.
-    assert sel("N", "T", 3072, 3072, 3072) == "mfma32_256x128x32_w4x2_streamk"
-    assert sel("T", "N", 3072, 3072, 3072) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    assert sel("N", "T", 3328, 3328, 3328) == "mfma32_256x128x32_w4x2_streamk"
+    assert sel("T", "N", 3328, 3328, 3328) == "mfma16_128x128x32_w4x2_streamk_1wg"
     assert sel("T", "T", 2560, 2560, 2560) == "mfma16_128x128x32_w4x2_streamk_1wg"
     assert sel("T", "N", 3584, 4096, 1024) == "mfma16_128x128x32_w4x2_streamk_1wg"
     # K <= 256 over at least 128 tiles of 64 x 64: the plain 64 x 64 tile.

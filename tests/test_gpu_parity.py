@@ -142,6 +142,12 @@ INT_CASES = [
     # The 256 x 256 tiles for the transposed op pairs (direct-to-LDS for TN and TT).
     *[W.Case(f"int_{ta}{tb}_4096x4096x512".lower(), ta, tb, 4096, 4096, 512, 1.0, -1.0, seed=77, fill="int_rand")
       for ta, tb in (("N", "T"), ("T", "N"), ("T", "T"))],
+    # The 192 x 192 tile for every op pair (256 tiles), and on a grid whose edge
+    # tiles cross M and N (clamped loads) with a k tail.
+    *[W.Case(f"int_{ta}{tb}_3072x3072x512".lower(), ta, tb, 3072, 3072, 512, 1.0, -1.0, seed=78, fill="int_rand")
+      for ta in "NT" for tb in "NT"],
+    *[W.Case(f"int_{ta}{tb}_3000x2900x700".lower(), ta, tb, 3000, 2900, 700, 2.0, -1.0, seed=79, fill="int_rand")
+      for ta, tb in (("N", "N"), ("T", "T"))],
 ]
 
 
@@ -384,10 +390,12 @@ def test_clamped_edge_tiles(config, ta, tb, layout):
     ("T", "T", 2048, 4096, 1024, "offset", "mfma16_128x128x32_w4x2"),
     ("N", "T", 2048, 4096, 1024, "offset", "mfma16_128x128x32_w4x2"),
     ("N", "N", 2000, 2000, 2001, "odd_ld", "mfma16_128x128x32_w4x2"),
+    ("N", "N", 3072, 3072, 1024, "offset", "mfma16_192x192x32_w4x3"),
+    ("T", "T", 3000, 2900, 700, "odd_ld", "mfma16_192x192x32_w4x3"),
 ])
 def test_unaligned_operands_on_substituted_tiles(ta, tb, M, N, K, layout, aligned_pick):
     """Shapes whose pick for 16-byte-loadable operands is a tile without a
-    4-byte straight-line form for that op pair (the 256 x 256 and
+    4-byte straight-line form for that op pair (the 256 x 256, 192 x 192 and
     128 x 256 x 16 tiles, the two-workgroup stream-K tile, the 16 x 16
     128 x 128 w4x2 tile except NT): with unaligned operands mi_sgemm runs a
     substitute with 4-byte straight-line rounds. Bit-exact on integer inputs."""
