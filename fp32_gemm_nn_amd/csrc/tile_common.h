@@ -86,7 +86,8 @@ struct TileCfg {
     static_assert(BK % (2 * QK) == 0, "fragment buffers alternate, so a k-tile holds an even number of q-groups");
 };
 
-// n adjacent floats from LDS (n = 1, 2, 4), as one ds_read.
+// n adjacent floats from LDS: one ds_read for n = 1, 2, 4; n = 3 (three
+// blocks per lane row) is split by the compiler into a two- and a one-dword read.
 template <int n> struct LdsVec;
 template <> struct LdsVec<1> {
     static __device__ __forceinline__ void get(const float *p, float *out) { out[0] = *p; }

@@ -94,8 +94,8 @@ struct Frag {
 template <class CFG, bool TA, bool TB>
 struct Frag16 {
     static constexpr int FM = CFG::FM, FN = CFG::FN, WTM = CFG::WTM, WTN = CFG::WTN;
-    static_assert(!TA || (FM >= 1 && FM <= 4), "one LDS read covers a row's FM blocks");
-    static_assert(TB || (FN >= 1 && FN <= 4), "one LDS read covers a row's FN blocks");
+    static_assert(!TA || (FM >= 1 && FM <= 4), "one LdsVec read covers a row's FM blocks");
+    static_assert(TB || (FN >= 1 && FN <= 4), "one LdsVec read covers a row's FN blocks");
     float a[FM][4];
     float b[FN][4];
 
