@@ -34,11 +34,12 @@
 //   * Edges: a k-tile that crosses K takes a guarded load path that reads
 //     only in-range elements and selects zero for the rest (the zero-fill of
 //     the klklkl10086 page, 01-Shared Memory Tiling); so do the edge tiles of
-//     the 256 x 256 tile, and all its tiles when A or B cannot be read with
+//     the 256 x 256 tiles, and all its tiles when A or B cannot be read with
 //     16-byte loads. The other tiles keep the straight-line rounds for every
 //     complete k-tile with clamped loads (16-byte, or 4-byte in a separate
 //     instantiation for unaligned operands), whose extra values only reach
-//     outputs beyond M or N. Stores are masked to i < M, j < N.
+//     outputs beyond M or N, and load the k tail the same way with the
+//     elements past K selected to zero. Stores are masked to i < M, j < N.
 //   * Epilogue: C = alpha*acc + beta*C fused into the store (itan.pw page,
 //     sections 3.4-3.5); when beta == 0, C is not read, else a batch of C
 //     values is loaded before any of them is stored.

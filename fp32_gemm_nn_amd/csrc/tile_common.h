@@ -196,6 +196,38 @@ struct TileCopy {
         }
     }
 
+    // The k-tail tile (its k extent shorter than the tile's), without
+    // branches: loaded as load_clamped does, then every element at or beyond
+    // the k extent is set to zero, since those enter the sum of every output.
+    // K_ROWS: k runs along the tile's rows (rows_left is the k extent) rather
+    // than its columns (cols_left is). A 16-byte chunk that starts below the
+    // k extent is read whole: it starts 16-byte aligned inside its row, so it
+    // stays inside the row's ld floats and its page.
+    template <bool VEC, bool K_ROWS>
+    __device__ __forceinline__ void load_ktail(const float *__restrict__ base, int ld, int rows_left, int cols_left,
+                                               int tid) {
+        const int last_c = ((cols_left - 1) >> 2) << 2;
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int idx = tid + NT * j;
+            const int r = idx / CPR, c = (idx % CPR) * 4;
+            const int rr = r < rows_left ? r : rows_left - 1;
+            f32x4 t;
+            if constexpr (VEC) {
+                const int cc = c <= last_c ? c : last_c;
+                t = *reinterpret_cast<const f32x4 *>(base + (size_t)rr * ld + cc);
+            } else {
+                const float *p = base + (size_t)rr * ld;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) t[e] = p[c + e < cols_left ? c + e : cols_left - 1];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (K_ROWS ? r >= rows_left : c + e >= cols_left) t[e] = 0.0f;
+            v[j] = t;
+        }
+    }
+
     __device__ __forceinline__ void store(float *lds, int tid) const {
 #pragma unroll
         for (int j = 0; j < PER_THREAD; ++j) {

@@ -332,14 +332,29 @@ void sgemm_mfma32(GemmArgs g) {
                     fetch_fast(kt);
                     return;
                 }
+                if (wg_fast) {
+                    // The k tail (kt == kfull, K not a multiple of BK): clamped
+                    // loads with the elements past K zeroed. The thread id is
+                    // made opaque so that these addresses are formed here
+                    // rather than held through the k-loop.
+                    int ltid = gtid;
+                    asm volatile("" : "+v"(ltid));
+                    const int kleft = K - kt * BK;
+                    ca.template load_ktail<!SCALAR, TA>(a_ptr + kt * a_step, g.lda, TA ? kleft : a_rows,
+                                                        TA ? a_cols : kleft, ltid);
+                    cb.template load_ktail<!SCALAR, !TB>(b_ptr + kt * b_step, g.ldb, TB ? b_rows : kleft,
+                                                         TB ? kleft : b_cols, ltid);
+                    return;
+                }
             }
             const int k0 = kt * BK;
             // Complete k-tiles of interior workgroups unguarded (the only ones
             // left fast without edge clamping), the rest guarded. Rows/cols
             // left counted from this k-tile's origin.
             const bool guard = CLAMP_EDGE || !(wg_fast && kt < kfull);
-            // Tiles that clamp their edges reach this only for the k-tail
-            // round: with the thread id made opaque here its element addresses
+            // Tiles that clamp their edges reach this only when their operands
+            // allow no 16-byte loads and they have no 4-byte straight-line
+            // form: with the thread id made opaque here its element addresses
             // are formed when needed instead of being held through the k-loop.
             int ltid = gtid;
             if constexpr (CLAMP_EDGE) asm volatile("" : "+v"(ltid));

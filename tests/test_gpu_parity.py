@@ -146,8 +146,15 @@ INT_CASES = [
     # tiles cross M and N (clamped loads) with a k tail.
     *[W.Case(f"int_{ta}{tb}_3072x3072x512".lower(), ta, tb, 3072, 3072, 512, 1.0, -1.0, seed=78, fill="int_rand")
       for ta in "NT" for tb in "NT"],
-    *[W.Case(f"int_{ta}{tb}_3000x2900x700".lower(), ta, tb, 3000, 2900, 700, 2.0, -1.0, seed=79, fill="int_rand")
-      for ta, tb in (("N", "N"), ("T", "T"))],
+    *[W.Case(f"int_{ta}{tb}_3000x2900x{k}".lower(), ta, tb, 3000, 2900, k, 2.0, -1.0, seed=79, fill="int_rand")
+      for ta, tb, k in (("N", "N", 700), ("T", "T", 701))],
+    # k tails of every length mod 4 on the chosen kernels (zero-filled clamped
+    # loads of the last k-tile): split-K, k-groups, stream-K.
+    W.Case("int_nn_1000x1300x703", "N", "N", 1000, 1300, 703, 1.0, 1.0, seed=80, fill="int_rand"),
+    *[W.Case(f"int_{ta}{tb}_1024x1024x1001".lower(), ta, tb, 1024, 1024, 1001, 1.0, -1.0, seed=81, fill="int_rand")
+      for ta, tb in (("T", "N"), ("N", "T"))],
+    W.Case("int_tn_1568x1124x949", "T", "N", 1568, 1124, 949, 1.0, 0.0, seed=82, fill="int_rand"),
+    W.Case("int_nn_2500x2500x2502", "N", "N", 2500, 2500, 2502, 0.5, 1.0, seed=83, fill="int_rand"),
 ]
 
 
@@ -363,8 +370,11 @@ def test_clamped_edge_tiles(config, ta, tb, layout):
     odd leading dimensions or pointers one float off 16 bytes: the 4-byte
     instantiation clamps every element into the matrix. Only outputs beyond M
     or N see the extra values; every stored output must equal the oracle's bit
-    for bit (integer inputs), with and without a k tail."""
-    for t, (M, N, K) in enumerate([(100, 76, 96), (5, 200, 128), (130, 3, 64), (100, 76, 100), (257, 129, 36)]):
+    for bit (integer inputs), with and without a k tail. The k tail (K mod 32
+    of 4, 3, 1 and 6 here) is loaded the same way with the elements past K
+    zeroed: a 16-byte chunk that straddles K reads NaN row padding beyond it."""
+    for t, (M, N, K) in enumerate([(100, 76, 96), (5, 200, 128), (130, 3, 64), (100, 76, 100), (257, 129, 36),
+                                   (100, 76, 99), (70, 130, 37), (66, 200, 102)]):
         case = W.Case(f"clamp_{layout}_{ta}{tb}_{M}x{N}x{K}_cfg{config}", ta, tb, M, N, K, 1.0 if t % 2 else 2.0,
                       0.0 if t % 2 else -1.0, seed=500 + t, fill="int_rand")
         note(case.name)
