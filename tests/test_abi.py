@@ -162,7 +162,14 @@ def test_shape_class_selection():
     assert sel("T", "T", 2048, 4096, 1024) == "mfma16_128x128x32_w4x2"
     assert sel("N", "T", 2048, 4096, 1024) == "mfma16_128x128x32_w4x2"
     # 1024^2 output: 64 tiles of 128 x 128 only, so smaller tiles with four k-groups.
-    assert sel("N", "N", 1024, 1024, 1024) == "mfma16_64x64x32_w2x2_kg4"
+    # Four k-groups of two waves where the grid fills at least 224 CUs, A is not
+    # transposed and K has no tail; of four waves otherwise.
+    assert sel("N", "N", 1024, 1024, 1024) == "mfma16_64x64x32_w2x1_kg4"
+    assert sel("N", "T", 1024, 1024, 1024) == "mfma16_64x64x32_w2x1_kg4"
+    assert sel("T", "N", 1024, 1024, 1024) == "mfma16_64x64x32_w2x2_kg4"
+    assert sel("N", "N", 1024, 1024, 1000) == "mfma16_64x64x32_w2x2_kg4"
+    assert sel("N", "N", 1024, 896, 1024) == "mfma16_64x64x32_w2x1_kg4"
+    assert sel("N", "N", 1024, 832, 1024) == "mfma16_64x64x32_w2x2_kg4"
     assert sel("N", "N", 1000, 1300, 700) == "mfma16_64x64x32_w2x2_splitk"
     # 257..511 tiles of 64 x 64 filling 75-85% of two slots per CU, with enough
     # k-work and B not transposed: stream-K over 128 x 128 tiles; fuller grids,
@@ -181,7 +188,7 @@ def test_shape_class_selection():
     assert sel("N", "N", 768, 768, 768) == "mfma16_64x64x32_w2x2_splitk"
     assert sel("T", "T", 832, 832, 832) == "mfma16_64x64x32_w2x2_splitk"
     assert sel("N", "N", 2048, 256, 2048) == "mfma16_64x64x32_w2x2_splitk"
-    assert sel("N", "N", 960, 960, 960) == "mfma16_64x64x32_w2x2_kg4"
+    assert sel("N", "N", 960, 960, 960) == "mfma16_64x64x32_w2x1_kg4"
     # 361 tiles fill under 75% of two slots per CU: split-K.
     assert sel("N", "N", 1216, 1216, 1216) == "mfma16_64x64x32_w2x2_splitk"
     # 144..255 tiles of 128 x 128 with enough k-work: stream-K, one workgroup per CU.

@@ -135,6 +135,7 @@ def test_square_sweep(n):
 INT_CASES = [
     W.C1.with_(name="int_c1", fill="int_trunc"),
     W.C2.with_(name="int_floor_1024", fill="int_floor"),
+    W.C2.with_(name="int_nt_1024", transB="T", fill="int_rand", beta=-1.0),
     W.C4.with_(name="int_4096", fill="int_trunc"),
     W.C5B.with_(name="int_skinny", fill="int_rand"),
     *[c.with_(name="int_" + c.name, fill="int_rand", alpha=2.0, beta=-1.0) for c in W.C5A],
