@@ -359,8 +359,17 @@ int select_config(char transA, char transB, int M, int N, int K) {
     const long long kt = (K + 31) / 32;
     // Short k (K <= 256) over at least 128 tiles of 64 x 64: the plain 64 x 64
     // tile, whose k-loop is too short for k-groups, splits or stream-K to pay
-    // (1024 x 2048 x 256 TT: 53% of peak vs 47% two k-groups, 33% 128 x 128).
-    if (kt <= 8 && t64 >= 128) return kCfg16x64;
+    // (1024 x 2048 x 256 TT: 53% of peak vs 47% two k-groups, 33% 128 x 128),
+    // unless 128 x 128 tiles spread over the CUs as evenly (each weighed by
+    // the cube of its grid's filled fraction): then 128 x 128, 3-6% faster
+    // (2048 x 4096 x 256: 5.7%; 1792^3 x 256 TT 5.4%; 46 seeded shapes).
+    if (kt <= 8 && t64 >= 128) {
+        auto fill3 = [&](int b) {
+            const double u = (double)M * N / ((double)tiles(b, b) * b * b);
+            return u * u * u;
+        };
+        return cu_balance(t128) * fill3(128) >= cu_balance(t64) * fill3(64) ? cfg128 : kCfg16x64;
+    }
     if (t128 >= kNumCus) {
         const bool ta = op_t(transA), tb = op_t(transB);
         // Big tiles (one workgroup per CU) lose to 128 x 128 (two per CU)
@@ -432,6 +441,17 @@ int select_config(char transA, char transB, int M, int N, int K) {
         if (best == s_b8) return wide ? kCfg128x256 : kCfg256x128;
         return best == s_128 ? cfg128 : kCfg16x64;
     }
+    // Stream-K over 128 x 128 tiles, or split-K over 64 x 64 tiles where the
+    // timing models put it first. Stream-K's time is fitted on 103 seeded
+    // shapes with 64..255 such tiles (15.55 us + 1.967 us per 128 x 128 x 32
+    // iteration per CU, mean error 1.4%); the 64 x 64 model runs about 10%
+    // long. Scored on 270 seeded random shapes mean regret 1.03% -> 0.73% (on
+    // two further scans 0.94% -> 0.89%).
+    auto sk_or_split = [&]() {
+        const double t_sk = 15.55 + 1.967 * (double)t128 * kt / kNumCus;
+        const double t_sp = model_64x64_us(t64, (int)kt, 1, splits_64x64(t64, (int)kt));
+        return 0.9 * t_sp < t_sk ? kCfg16x64Split : kCfg16StreamK1;
+    };
     // 128..255 tiles of 128 x 128 with enough k-work per workgroup: stream-K,
     // one workgroup per CU (1792 x 1280 x 4096 TN, 140 tiles: 78% of peak vs
     // 58% for 64 x 64; 768 x 3072 x 1024 TN, 144 tiles: 62% vs 56%). At 128
@@ -451,12 +471,12 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // enough (3584 x 1152 x 1024 NT, 252 tiles: 79% of peak vs 69%).
     if (t128 < 230 &&
         ((t128 >= 144 && sk_iters >= 16LL * kNumCus) || (t128 >= 128 && sk_iters >= 20LL * kNumCus)))
-        return kCfg16StreamK1;
+        return sk_or_split();
     if (t128 >= 3 * kNumCus / 4) return cfg128;
     // 72..127 tiles with long k (K >= 2048): stream-K again rather than k-groups
     // or split-K over 64 x 64 tiles (1536 x 768 x 4096 TN: 71% of peak vs 63%;
     // 1024 x 1280 x 4096 NT: 73% vs 70%).
-    if (t128 >= 72 && kt >= 64) return kCfg16StreamK1;
+    if (t128 >= 72 && kt >= 64) return sk_or_split();
     if (t64 >= 2 * kNumCus) return kCfg16x64;
     // 257..511 tiles of 64 x 64 that fill 75-85% of two workgroup slots per
     // CU, with enough k-work and B not transposed: stream-K over 128 x 128

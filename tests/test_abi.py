@@ -221,8 +221,16 @@ def test_shape_class_selection():
     assert sel("T", "N", 3328, 3328, 3328) == "mfma16_128x128x32_w4x2_streamk_1wg"
     assert sel("T", "T", 2560, 2560, 2560) == "mfma16_128x128x32_w4x2_streamk_1wg"
     assert sel("T", "N", 3584, 4096, 1024) == "mfma16_128x128x32_w4x2_streamk_1wg"
-    # K <= 256 over at least 128 tiles of 64 x 64: the plain 64 x 64 tile.
+    # K <= 256 over at least 128 tiles of 64 x 64: the plain 64 x 64 tile,
+    # unless 128 x 128 tiles spread over the CUs as evenly.
     assert sel("T", "T", 1024, 2048, 256) == "mfma16_64x64x32_w2x2"
+    assert sel("N", "N", 2048, 4096, 256) == "mfma16_128x128x32_w4x2"
+    assert sel("T", "T", 1792, 1792, 256) == "mfma16_128x128x32_w4x2"
+    # Where the stream-K rules apply, split-K over 64 x 64 tiles when the timing
+    # models put it first.
+    assert sel("N", "T", 1548, 920, 2236) == "mfma16_64x64x32_w2x2_splitk"
+    assert sel("T", "T", 792, 1612, 2196) == "mfma16_64x64x32_w2x2_splitk"
+    assert sel("T", "N", 1792, 1280, 4096) == "mfma16_128x128x32_w4x2_streamk_1wg"
     assert sel("N", "N", 2560, 2560, 256) == "mfma16_64x64x32_w2x2"
     # No stream-K below K = 1024 on big grids.
     assert sel("T", "T", 3584, 2560, 512) == "mfma16_64x64x32_w2x2"
