@@ -584,7 +584,8 @@ def run_regret(path, shapes=90, seed=11, warmup=3, ragged=False):
     """Selection check on random shapes: M and N drawn from 768..4096, K from
     256..4096 (with ragged: M, N, K uniform over the multiples of 4 in
     512..4096), op pairs at random (seeded). Every matrix-core tile configuration
-    is timed on each shape (best of two runs of back-to-back calls, beta = 0)
+    is timed on each shape (best of two runs of back-to-back calls after 25 ms
+    of warm-up calls, beta = 0)
     and select_config's pick is scored by its regret against the fastest. One
     JSON object per shape, then a summary line."""
     import random
@@ -624,8 +625,15 @@ def run_regret(path, shapes=90, seed=11, warmup=3, ragged=False):
                 for cfg in tile_cfgs:
                     args = (ta, tb, M, N, K, 1.0, A.data_ptr(), A.shape[1], B.data_ptr(), B.shape[1], 0.0,
                             C.data_ptr(), N, h)
-                    for _ in range(warmup):
-                        mg.mi_sgemm_with_config(cfg, *args)
+                    # At least `warmup` calls and 25 ms of them: the shader clock
+                    # takes about 20 ms to ramp back up after a configuration that
+                    # loads only part of the chip.
+                    t0, calls = time.perf_counter(), 0
+                    while calls < warmup or time.perf_counter() - t0 < 0.025:
+                        for _ in range(10):
+                            mg.mi_sgemm_with_config(cfg, *args)
+                        stream.synchronize()
+                        calls += 10
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
                     for _ in range(n):
