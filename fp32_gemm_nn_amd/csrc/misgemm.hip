@@ -127,6 +127,7 @@ using Cfg16L42D = TileCfg<128, 128, 32, 4, 2, 1, 4, false, false, true, true>;
 using Cfg16S4D = TileCfg<64, 64, 32, 2, 2, 4, 0, false, false, true, true>;
 using Cfg16Q12 = TileCfg<192, 192, 32, 4, 3, 1, 0, false, false, false, true>;   // 12 waves, 48 x 64 per wave
 using Cfg16S4W = TileCfg<64, 64, 32, 2, 1, 4, 0, false, false, false, true>;      // 4 k-groups of 2 waves, 32 x 64 per wave
+using Cfg16L42S2 = TileCfg<128, 128, 32, 4, 2, 1, 4, false, true, false, true>;   // stream-K, two workgroups per CU
 
 // Config ids: the index of each entry of kConfigs below.
 enum ConfigId : int {
@@ -167,6 +168,7 @@ enum ConfigId : int {
     kCfg16x64Kg4Dl = 36,
     kCfg16x192W43 = 37,
     kCfg16x64W21Kg4 = 38,
+    kCfg16StreamK2 = 39,
 };
 
 struct ConfigInfo {
@@ -214,10 +216,11 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma16_64x64x32_w2x2_kg4_dl", Cfg16S4D::BM, Cfg16S4D::BN, Cfg16S4D::NT},
     {"mfma16_192x192x32_w4x3", Cfg16Q12::BM, Cfg16Q12::BN, Cfg16Q12::NT},
     {"mfma16_64x64x32_w2x1_kg4", Cfg16S4W::BM, Cfg16S4W::BN, Cfg16S4W::NT},
+    {"mfma16_128x128x32_w4x2_streamk_2wg", Cfg16L42S2::BM, Cfg16L42S2::BN, Cfg16L42S2::NT},
 };
 constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-static_assert(kNumConfigs == kCfg16x64W21Kg4 + 1, "one ConfigId per kConfigs entry");
+static_assert(kNumConfigs == kCfg16StreamK2 + 1, "one ConfigId per kConfigs entry");
 static_assert(kCfgLadderLast + 1 == kCfg256x256Dl, "the ladder ids are contiguous");
 static_assert(kConfigs[kCfg128].bm == CfgL::BM && kConfigs[kCfg128].bn == CfgL::BN && kConfigs[kCfg128].nt == CfgL::NT, "kConfigs order");
 static_assert(kConfigs[kCfg64].bm == CfgS::BM && kConfigs[kCfg64].bn == CfgS::BN && kConfigs[kCfg64].nt == CfgS::NT, "kConfigs order");
@@ -434,7 +437,12 @@ int select_config(char transA, char transB, int M, int N, int K) {
                                  fmax(fmax(fmax(s_128, s_64), s_sk16), s_192));
         if (best == s_q) return ta ? kCfg256x256Dl : kCfg256x256;
         if (best == s_192) return kCfg16x192W43;
-        if (best == s_sk16) return kCfg16StreamK1;
+        // With neither operand transposed and at least 400 tiles of 128 x 128,
+        // two stream-K workgroups per CU (four waves per SIMD): 3328^3-3840^3
+        // 1.5-2.6% faster, 2560^3 0.8%, 30 seeded shapes of 400-1428 tiles
+        // +1.2% on average, NN ones +0.3% to +6.1%; with A transposed it was
+        // up to 5% slower, and below two waves of tiles (n <= 1792) 4-18%.
+        if (best == s_sk16) return (!ta && !tb && t128 >= 400) ? kCfg16StreamK2 : kCfg16StreamK1;
         if (best == s_skb) return wide ? kCfgStreamK128x256 : kCfgStreamK256x128;
         if (best == s_sk) return kCfgStreamK2;
         if (best == s_b4) return kCfg128x256x16;
@@ -512,14 +520,15 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Whether the tile has a 4-byte straight-line instantiation for this op pair:
 // every clamping tile, except the forms whose clamped element addresses do
 // not fit the register budget (they spilled: the 128 x 256 x 16 tile, the
-// two-workgroup stream-K tile, the 16 x 16 128 x 128 w4x2 tile other than NT,
-// and the 32 x 32 128 x 128 w2x4 / w4x2 tiles for TN). mi_sgemm routes
+// two-workgroup stream-K tiles, the 16 x 16 128 x 128 w4x2 tile other than NT,
+// and the 32 x 32 128 x 128 w2x4 / w4x2 tiles for TN), and the 192 x 192
+// tile, whose edge tiles clamp but which has no 4-byte form. mi_sgemm routes
 // operands without 16-byte loads away from these tiles (unaligned_substitute);
 // when one is forced, it runs the guarded rounds.
 template <class CFG, bool TA, bool TB>
 constexpr bool kScalarForm =
     kClampEdge<CFG> && !std::is_same_v<CFG, CfgT16> && !std::is_same_v<CFG, CfgL42S2> &&
-    !std::is_same_v<CFG, Cfg16Q12> &&
+    !std::is_same_v<CFG, Cfg16Q12> && !std::is_same_v<CFG, Cfg16L42S2> &&
     !(std::is_same_v<CFG, Cfg16L42> && !(!TA && TB)) &&
     !((std::is_same_v<CFG, CfgL24> || std::is_same_v<CFG, CfgL42>) && TA && !TB);
 
@@ -529,8 +538,9 @@ constexpr bool kScalarForm =
 // TT on 128 x 256: 1006 against 1253); for the others the replacement was the
 // fastest measured (MI355X, pointers one float off 16 bytes):
 //   128 x 256 x 16 -> 256 x 128 / 128 x 256   (4000^3 NN: 982 us vs 1046)
-//   two-workgroup stream-K -> 16 x 16 stream-K (2304 x 2304 x 1024 NT: 97.9 vs
-//                                              106.0 us; TT: 106.2 vs 117.4)
+//   two-workgroup stream-K (32 x 32 or 16 x 16 blocks), 192 x 192
+//                              -> 16 x 16 stream-K (2304 x 2304 x 1024 NT: 97.9
+//                                 vs 106.0 us; TT: 106.2 vs 117.4)
 //   16 x 16 128 x 128 w4x2 (not NT) -> 256 x 128 on a grid it fills evenly
 //                                     (2048 x 4096 x 1024 NN / TN / TT: 136 /
 //                                     145 / 139 us vs 153 / 174 / 176), else
@@ -544,6 +554,7 @@ int unaligned_substitute(int config, bool ta, bool tb, int M, int N) {
         case kCfg256x256Dl: return (ta && tb) ? kCfg128x256 : kCfg256x128;
         case kCfg128x256x16: return wide && !(ta && tb) ? kCfg128x256 : kCfg256x128;
         case kCfgStreamK2:
+        case kCfg16StreamK2:
         case kCfg16x192W43: return kCfg16StreamK1;
         case kCfg16x128W42:
             if (!ta && tb) return config;
@@ -971,6 +982,7 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case kCfg16x64Kg4Dl: err = launch_cfg<Cfg16S4D>(ta, tb, g, stream, wsrc); break;
         case kCfg16x192W43: err = launch_cfg<Cfg16Q12>(ta, tb, g, stream, wsrc); break;
         case kCfg16x64W21Kg4: err = launch_cfg<Cfg16S4W>(ta, tb, g, stream, wsrc); break;
+        case kCfg16StreamK2: err = launch_cfg<Cfg16L42S2>(ta, tb, g, stream, wsrc); break;
         default: err = launch_cfg<CfgTS>(ta, tb, g, stream, wsrc); break;   // kCfgStreamK128x256
     }
     if (wsrc.overflow) return MISGEMM_SCRATCH_TOO_SMALL;

@@ -131,6 +131,10 @@ def test_selection_fuzz():
         # (the register-staged one spills for TT and is slower for TN).
         if ta in "TtCc":
             assert name != "mfma32_256x256x32_w4x2", (ta, tb, M, N, K, name)
+        # The 16 x 16 two-workgroup stream-K tile only with neither operand
+        # transposed (its TT form spills).
+        if name == "mfma16_128x128x32_w4x2_streamk_2wg":
+            assert ta in "Nn" and tb in "Nn", (ta, tb, M, N, K, name)
 
 
 def test_shape_class_selection():
@@ -201,8 +205,10 @@ def test_shape_class_selection():
     skw = "mfma32_256x128x32_w4x2_streamk"
     sk16 = "mfma16_128x128x32_w4x2_streamk_1wg"
     q192 = "mfma16_192x192x32_w4x3"
-    for n, want in [(2048, "mfma16_128x128x32_w4x2"), (2304, sk16), (2560, sk16), (2816, "mfma32_256x128x32_w4x2"),
-                    (3072, q192), (3328, sk16), (3584, sk16), (3840, sk16), (4096, "mfma32_256x256x32_w4x2"),
+    # From 400 tiles of 128 x 128, NN takes two 16 x 16 stream-K workgroups per CU.
+    sk16b = "mfma16_128x128x32_w4x2_streamk_2wg"
+    for n, want in [(2048, "mfma16_128x128x32_w4x2"), (2304, sk16), (2560, sk16b), (2816, "mfma32_256x128x32_w4x2"),
+                    (3072, q192), (3328, sk16b), (3584, sk16b), (3840, sk16b), (4096, "mfma32_256x256x32_w4x2"),
                     (6144, q192), (8192, "mfma32_256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == want, n
     # The 192 x 192 tile where its grid fills at least 88% of a whole number of
@@ -264,8 +270,10 @@ def test_shape_class_selection():
     assert sel("N", "T", 1072, 2768, 764) == "mfma16_64x64x32_w2x2"
     assert sel("N", "N", 1536, 2048, 512) == "mfma16_64x64x32_w2x2"
     assert sel("N", "T", 2304, 2304, 1024) == "mfma32_128x128x32_w4x2_streamk_2wg"
-    # N > M: NN takes the 16 x 16 stream-K tile; transposed B keeps the 128 x 256 stream-K tile.
-    assert sel("N", "N", 2304, 3328, 2048) == "mfma16_128x128x32_w4x2_streamk_1wg"
+    # N > M: NN takes the 16 x 16 stream-K tile (two per CU from 400 tiles); transposed B keeps the
+    # 128 x 256 stream-K tile.
+    assert sel("N", "N", 2304, 3328, 2048) == "mfma16_128x128x32_w4x2_streamk_2wg"
+    assert sel("N", "N", 2304, 2304, 2048) == "mfma16_128x128x32_w4x2_streamk_1wg"
     assert sel("N", "T", 2304, 3328, 2048) == "mfma32_128x256x32_w2x4_streamk"
     # M <= 32: the skinny, bandwidth-bound kernel.
     assert "skinny" in sel("N", "N", 16, 4096, 4096)

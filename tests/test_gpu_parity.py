@@ -156,6 +156,8 @@ INT_CASES = [
       for ta, tb in (("T", "N"), ("N", "T"))],
     W.Case("int_tn_1568x1124x949", "T", "N", 1568, 1124, 949, 1.0, 0.0, seed=82, fill="int_rand"),
     W.Case("int_nn_2500x2500x2502", "N", "N", 2500, 2500, 2502, 0.5, 1.0, seed=83, fill="int_rand"),
+    # Two 16 x 16 stream-K workgroups per CU (520 tiles of 128 x 128, k tail).
+    W.Case("int_nn_3328x2560x1000", "N", "N", 3328, 2560, 1000, 1.0, -1.0, seed=84, fill="int_rand"),
 ]
 
 

@@ -9,10 +9,11 @@ section „Çà„Åè„ÅÇ„ÇãËêΩ„Å®„ÅóÁ©¥„Å®„ÉÅ„Çß„ÉÉ„ÇØ„É™„Çπ„Éà, item 4, ÈÅéÂ∫¶„Å™„É¨„Ç
 registers go to slow local memory).
 
 No instantiation the shape-class selection can reach may spill, for any op
-pair, aligned or not. One forced-only instantiation is allowed to: the
+pair, aligned or not. Two forced-only instantiations are allowed to: the
 register-staged 256 x 256 tile with both operands transposed (with A
-transposed the selection takes the direct-to-LDS form); test_abi's selection
-fuzz checks that it is never chosen.
+transposed the selection takes the direct-to-LDS form) and the 16 x 16
+two-workgroup stream-K tile with both transposed (selected for NN only);
+test_abi's selection fuzz checks that neither is chosen.
 """
 import os
 
@@ -27,6 +28,9 @@ msgpack = pytest.importorskip("msgpack")
 # TileCfg<256,256,32,4,2,1,0,false,false,false,false> with TA = TB = true.
 FORCED_ONLY_SPILLING = {
     "TileCfgILi256ELi256ELi32ELi4ELi2ELi1ELi0ELb0ELb0ELb0ELb0EEELb1ELb1ELb0E": "256x256 register-staged, TT",
+    # TileCfg<128,128,32,4,2,1,4,false,true,false,true> (16 x 16 stream-K, two
+    # workgroups per CU) with TA = TB = true: selected only for NN.
+    "TileCfgILi128ELi128ELi32ELi4ELi2ELi1ELi4ELb0ELb1ELb0ELb1EEELb1ELb1ELb0E": "16x16 stream-K 2 WG/CU, TT",
 }
 
 

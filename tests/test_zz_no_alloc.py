@@ -62,6 +62,7 @@ PAIRS = [
     ("band", W.C5B, W.Case("band_small", "N", "N", 9, 1024, 2048, 1.0, 1.0, seed=81)),
     ("splitk64", W.C1, W.Case("splitk_small", "N", "N", 300, 500, 600, 1.5, 0.5, seed=82)),
     ("streamk16", W.c3(1536), W.Case("streamk16_small", "N", "N", 1280, 1280, 1280, 1.0, 0.0, seed=83)),
+    ("streamk16_2wg", W.c3(2560), W.Case("streamk16_2wg_small", "N", "N", 2304, 3328, 2048, 1.0, 1.0, seed=86)),
     ("streamk256x128", W.Case("nt_3328", "N", "T", 3328, 3328, 2048, 1.0, 0.0, seed=84),
      W.Case("nt_2304", "N", "T", 2304, 2304, 1024, 1.0, 1.0, seed=85)),
 ]
