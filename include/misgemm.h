@@ -132,7 +132,7 @@ int mi_sgemm_with_config(int config, char transA, char transB, int M, int N, int
  * when A and B allow 16-byte loads (16-byte aligned pointers, lda and ldb
  * multiples of 4); for other operands mi_sgemm replaces the tiles that have
  * no 4-byte straight-line form (the 256 x 256, 192 x 192 and 128 x 256 x 16
- * tiles, the two-workgroup stream-K tile, and the 16 x 16 128 x 128 w4x2 tile
+ * tiles, the two-workgroup stream-K tiles, and the 16 x 16 128 x 128 w4x2 tile
  * except for NT) by a 256 x 128, 128 x 256 or 16 x 16 stream-K tile. Host-side decision
  * only; no HIP call.
  * Returns a negative status for invalid trans letters or negative sizes.
