@@ -404,12 +404,13 @@ def test_clamped_edge_tiles(config, ta, tb, layout):
     ("N", "T", 2048, 4096, 1024, "offset", "mfma16_128x128x32_w4x2"),
     ("N", "N", 2000, 2000, 2001, "odd_ld", "mfma16_128x128x32_w4x2"),
     ("N", "N", 3072, 3072, 1024, "offset", "mfma16_192x192x32_w4x3"),
+    ("N", "N", 3328, 2560, 1000, "odd_ld", "mfma16_128x128x32_w4x2_streamk_2wg"),
     ("T", "T", 3000, 2900, 700, "odd_ld", "mfma16_192x192x32_w4x3"),
 ])
 def test_unaligned_operands_on_substituted_tiles(ta, tb, M, N, K, layout, aligned_pick):
     """Shapes whose pick for 16-byte-loadable operands is a tile without a
     4-byte straight-line form for that op pair (the 256 x 256, 192 x 192 and
-    128 x 256 x 16 tiles, the two-workgroup stream-K tile, the 16 x 16
+    128 x 256 x 16 tiles, the two-workgroup stream-K tiles, the 16 x 16
     128 x 128 w4x2 tile except NT): with unaligned operands mi_sgemm runs a
     substitute with 4-byte straight-line rounds. Bit-exact on integer inputs."""
     assert mg.config_names()[mg.mi_sgemm_select_config(ta, tb, M, N, K)] == aligned_pick
