@@ -128,6 +128,7 @@ using Cfg16S4D = TileCfg<64, 64, 32, 2, 2, 4, 0, false, false, true, true>;
 using Cfg16Q12 = TileCfg<192, 192, 32, 4, 3, 1, 0, false, false, false, true>;   // 12 waves, 48 x 64 per wave
 using Cfg16S4W = TileCfg<64, 64, 32, 2, 1, 4, 0, false, false, false, true>;      // 4 k-groups of 2 waves, 32 x 64 per wave
 using Cfg16L42S2 = TileCfg<128, 128, 32, 4, 2, 1, 4, false, true, false, true>;   // stream-K, two workgroups per CU
+using Cfg16L42K2 = TileCfg<128, 128, 32, 4, 2, 2, 0, false, false, false, true>;   // 2 k-groups of 8 waves
 
 // Config ids: the index of each entry of kConfigs below.
 enum ConfigId : int {
@@ -169,6 +170,7 @@ enum ConfigId : int {
     kCfg16x192W43 = 37,
     kCfg16x64W21Kg4 = 38,
     kCfg16StreamK2 = 39,
+    kCfg16x128W42Kg2 = 40,
 };
 
 struct ConfigInfo {
@@ -217,10 +219,11 @@ constexpr ConfigInfo kConfigs[] = {
     {"mfma16_192x192x32_w4x3", Cfg16Q12::BM, Cfg16Q12::BN, Cfg16Q12::NT},
     {"mfma16_64x64x32_w2x1_kg4", Cfg16S4W::BM, Cfg16S4W::BN, Cfg16S4W::NT},
     {"mfma16_128x128x32_w4x2_streamk_2wg", Cfg16L42S2::BM, Cfg16L42S2::BN, Cfg16L42S2::NT},
+    {"mfma16_128x128x32_w4x2_kg2", Cfg16L42K2::BM, Cfg16L42K2::BN, Cfg16L42K2::NT},
 };
 constexpr int kSkinnyMaxM = 32;
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-static_assert(kNumConfigs == kCfg16StreamK2 + 1, "one ConfigId per kConfigs entry");
+static_assert(kNumConfigs == kCfg16x128W42Kg2 + 1, "one ConfigId per kConfigs entry");
 static_assert(kCfgLadderLast + 1 == kCfg256x256Dl, "the ladder ids are contiguous");
 static_assert(kConfigs[kCfg128].bm == CfgL::BM && kConfigs[kCfg128].bn == CfgL::BN && kConfigs[kCfg128].nt == CfgL::NT, "kConfigs order");
 static_assert(kConfigs[kCfg64].bm == CfgS::BM && kConfigs[kCfg64].bn == CfgS::BN && kConfigs[kCfg64].nt == CfgS::NT, "kConfigs order");
@@ -358,7 +361,12 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // The 128 x 128 and 64 x 64 tiles run as 16 x 16 MFMA blocks, 2-18%
     // faster than as 32 x 32 blocks for every op pair (1024^3: 22 vs 24 us;
     // 2048 x 4096 x 1024 TN: 132 vs 144 us).
-    const int cfg128 = kCfg16x128W42;
+    // One round of 128 x 128 tiles (at most one per CU) with long k (K >= 2048):
+    // two k-groups of eight waves per tile (four waves per SIMD), 0.5-2.5%
+    // faster than one group (2048^3 NN 131.0 -> 129.6 us, TN 2048 x 2048 x 8192
+    // 498.9 -> 486.8); at K <= 1024, or with two tiles per CU, no faster or
+    // slower.
+    const int cfg128 = (t128 <= kNumCus && K >= 2048) ? kCfg16x128W42Kg2 : kCfg16x128W42;
     const long long kt = (K + 31) / 32;
     // Short k (K <= 256) over at least 128 tiles of 64 x 64: the plain 64 x 64
     // tile, whose k-loop is too short for k-groups, splits or stream-K to pay
@@ -520,15 +528,16 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Whether the tile has a 4-byte straight-line instantiation for this op pair:
 // every clamping tile, except the forms whose clamped element addresses do
 // not fit the register budget (they spilled: the 128 x 256 x 16 tile, the
-// two-workgroup stream-K tiles, the 16 x 16 128 x 128 w4x2 tile other than NT,
-// and the 32 x 32 128 x 128 w2x4 / w4x2 tiles for TN), and the 192 x 192
+// two-workgroup stream-K tiles, the 16 x 16 128 x 128 w4x2 tile other than NT
+// and its two-k-group form, and the 32 x 32 128 x 128 w2x4 / w4x2 tiles for
+// TN), and the 192 x 192
 // tile, whose edge tiles clamp but which has no 4-byte form. mi_sgemm routes
 // operands without 16-byte loads away from these tiles (unaligned_substitute);
 // when one is forced, it runs the guarded rounds.
 template <class CFG, bool TA, bool TB>
 constexpr bool kScalarForm =
     kClampEdge<CFG> && !std::is_same_v<CFG, CfgT16> && !std::is_same_v<CFG, CfgL42S2> &&
-    !std::is_same_v<CFG, Cfg16Q12> && !std::is_same_v<CFG, Cfg16L42S2> &&
+    !std::is_same_v<CFG, Cfg16Q12> && !std::is_same_v<CFG, Cfg16L42S2> && !std::is_same_v<CFG, Cfg16L42K2> &&
     !(std::is_same_v<CFG, Cfg16L42> && !(!TA && TB)) &&
     !((std::is_same_v<CFG, CfgL24> || std::is_same_v<CFG, CfgL42>) && TA && !TB);
 
@@ -548,6 +557,8 @@ constexpr bool kScalarForm =
 //                                     148.5 vs 151.1 us)
 int unaligned_substitute(int config, bool ta, bool tb, int M, int N) {
     const bool wide = M < N;
+    // The two-k-group 16 x 16 128 x 128 tile: as the one-group tile.
+    if (config == kCfg16x128W42Kg2) config = kCfg16x128W42;
     auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     switch (config) {
         case kCfg256x256:
@@ -983,6 +994,7 @@ int run(int config, char transA, char transB, int M, int N, int K, float alpha, 
         case kCfg16x192W43: err = launch_cfg<Cfg16Q12>(ta, tb, g, stream, wsrc); break;
         case kCfg16x64W21Kg4: err = launch_cfg<Cfg16S4W>(ta, tb, g, stream, wsrc); break;
         case kCfg16StreamK2: err = launch_cfg<Cfg16L42S2>(ta, tb, g, stream, wsrc); break;
+        case kCfg16x128W42Kg2: err = launch_cfg<Cfg16L42K2>(ta, tb, g, stream, wsrc); break;
         default: err = launch_cfg<CfgTS>(ta, tb, g, stream, wsrc); break;   // kCfgStreamK128x256
     }
     if (wsrc.overflow) return MISGEMM_SCRATCH_TOO_SMALL;

@@ -154,10 +154,12 @@ def test_shape_class_selection():
     assert sel("N", "N", 4000, 4000, 4000) == "mfma32_128x256x16_w2x2"
     assert sel("T", "T", 4000, 4000, 4000) == "mfma32_256x128x32_w4x2"
     assert sel("N", "N", 3800, 4000, 4000) == "mfma32_128x256x16_w2x2"
-    # 128 x 128 and 64 x 64 tiles run as 16 x 16 MFMA blocks, for every op pair.
-    assert sel("T", "N", 2048, 2048, 2048) == "mfma16_128x128x32_w4x2"
-    assert sel("T", "N", 2048, 2048, 4096) == "mfma16_128x128x32_w4x2"
-    assert sel("N", "N", 2048, 2048, 2048) == "mfma16_128x128x32_w4x2"
+    # 128 x 128 and 64 x 64 tiles run as 16 x 16 MFMA blocks, for every op pair;
+    # one round of 128 x 128 tiles with K >= 2048 as two k-groups of eight waves.
+    assert sel("T", "N", 2048, 2048, 2048) == "mfma16_128x128x32_w4x2_kg2"
+    assert sel("T", "N", 2048, 2048, 4096) == "mfma16_128x128x32_w4x2_kg2"
+    assert sel("N", "N", 2048, 2048, 2048) == "mfma16_128x128x32_w4x2_kg2"
+    assert sel("N", "N", 2048, 2048, 1024) == "mfma16_128x128x32_w4x2"
     # 2048 x 4096 x 1024: short K on a grid that fills the chip once: 128 x 128
     # (two workgroups per CU), for every op pair.
     assert sel("N", "N", 2048, 4096, 1024) == "mfma16_128x128x32_w4x2"
@@ -207,7 +209,7 @@ def test_shape_class_selection():
     q192 = "mfma16_192x192x32_w4x3"
     # From 400 tiles of 128 x 128, NN takes two 16 x 16 stream-K workgroups per CU.
     sk16b = "mfma16_128x128x32_w4x2_streamk_2wg"
-    for n, want in [(2048, "mfma16_128x128x32_w4x2"), (2304, sk16), (2560, sk16b), (2816, "mfma32_256x128x32_w4x2"),
+    for n, want in [(2048, "mfma16_128x128x32_w4x2_kg2"), (2304, sk16), (2560, sk16b), (2816, "mfma32_256x128x32_w4x2"),
                     (3072, q192), (3328, sk16b), (3584, sk16b), (3840, sk16b), (4096, "mfma32_256x256x32_w4x2"),
                     (6144, q192), (8192, "mfma32_256x256x32_w4x2")]:
         assert sel("N", "N", n, n, n) == want, n

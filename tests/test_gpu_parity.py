@@ -156,6 +156,9 @@ INT_CASES = [
       for ta, tb in (("T", "N"), ("N", "T"))],
     W.Case("int_tn_1568x1124x949", "T", "N", 1568, 1124, 949, 1.0, 0.0, seed=82, fill="int_rand"),
     W.Case("int_nn_2500x2500x2502", "N", "N", 2500, 2500, 2502, 0.5, 1.0, seed=83, fill="int_rand"),
+    # Two k-groups of eight waves on one round of 128 x 128 tiles (ragged M).
+    W.Case("int_tn_2016x2048x2048", "T", "N", 2016, 2048, 2048, 1.0, -1.0, seed=85, fill="int_rand"),
+    W.Case("int_nt_1920x2048x2100", "N", "T", 1920, 2048, 2100, 1.0, 0.0, seed=86, fill="int_rand"),
     # Two 16 x 16 stream-K workgroups per CU (520 tiles of 128 x 128, k tail).
     W.Case("int_nn_3328x2560x1000", "N", "N", 3328, 2560, 1000, 1.0, -1.0, seed=84, fill="int_rand"),
 ]
@@ -405,6 +408,7 @@ def test_clamped_edge_tiles(config, ta, tb, layout):
     ("N", "N", 2000, 2000, 2001, "odd_ld", "mfma16_128x128x32_w4x2"),
     ("N", "N", 3072, 3072, 1024, "offset", "mfma16_192x192x32_w4x3"),
     ("N", "N", 3328, 2560, 1000, "odd_ld", "mfma16_128x128x32_w4x2_streamk_2wg"),
+    ("T", "N", 2048, 2048, 2048, "offset", "mfma16_128x128x32_w4x2_kg2"),
     ("T", "T", 3000, 2900, 700, "odd_ld", "mfma16_192x192x32_w4x3"),
 ])
 def test_unaligned_operands_on_substituted_tiles(ta, tb, M, N, K, layout, aligned_pick):
