@@ -505,9 +505,13 @@ int select_config(char transA, char transB, int M, int N, int K) {
         t128 >= 96 && sk_iters >= 3000)
         return kCfg16StreamK1;
     // 257..511 tiles of 64 x 64: two k-groups unless their workgroups would
-    // leave the CU slots badly filled; then split-K over workgroups, whose
-    // smaller workgroups spread more evenly.
-    if (t64 > kNumCus) return (double)t64 / (2 * kNumCus) >= 0.75 ? kCfg16x64Kg2 : kCfg16x64Split;
+    // leave the CU slots badly filled, or the 64 x 64 timing model splits k
+    // (two or more splits: 384 tiles at K <= 1024); then split-K over
+    // workgroups, whose smaller workgroups spread more evenly (TT 2048 x 768 x
+    // 1024: 16.7% faster than two k-groups, NN 1536 x 1024 x 512 11.4%).
+    if (t64 > kNumCus)
+        return ((double)t64 / (2 * kNumCus) >= 0.75 && splits_64x64(t64, (int)kt) < 2) ? kCfg16x64Kg2
+                                                                                       : kCfg16x64Split;
     // Up to 256 tiles of 64 x 64: four k-groups or split-K over workgroups,
     // whichever the timing model puts first.
     const int ktiles = (K + 31) / 32;

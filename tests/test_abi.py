@@ -187,6 +187,9 @@ def test_shape_class_selection():
     assert sel("N", "T", 1280, 1280, 1280) == "mfma16_64x64x32_w2x2_kg2"
     assert sel("N", "N", 1280, 1280, 640) == "mfma16_64x64x32_w2x2_kg2"
     assert sel("N", "N", 1408, 1408, 1408) == "mfma16_64x64x32_w2x2_kg2"
+    # ... but split-K where the 64 x 64 timing model splits k (384 tiles, K <= 1024).
+    assert sel("T", "T", 2048, 768, 1024) == "mfma16_64x64x32_w2x2_splitk"
+    assert sel("N", "N", 1536, 1024, 512) == "mfma16_64x64x32_w2x2_splitk"
     assert sel("N", "N", 1792, 1024, 1024) == "mfma16_64x64x32_w2x2_kg2"
     assert sel("N", "N", 512, 512, 512) == "mfma16_64x64x32_w2x2_splitk"
     # Up to 256 tiles of 64 x 64: split-K where the 64 x 64 timing model puts
