@@ -374,13 +374,12 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // unless 128 x 128 tiles spread over the CUs as evenly (each weighed by
     // the cube of its grid's filled fraction): then 128 x 128, 3-6% faster
     // (2048 x 4096 x 256: 5.7%; 1792^3 x 256 TT 5.4%; 46 seeded shapes).
-    if (kt <= 8 && t64 >= 128) {
-        auto fill3 = [&](int b) {
-            const double u = (double)M * N / ((double)tiles(b, b) * b * b);
-            return u * u * u;
-        };
+    auto fill3 = [&](int b) {
+        const double u = (double)M * N / ((double)tiles(b, b) * b * b);
+        return u * u * u;
+    };
+    if (kt <= 8 && t64 >= 128)
         return cu_balance(t128) * fill3(128) >= cu_balance(t64) * fill3(64) ? cfg128 : kCfg16x64;
-    }
     if (t128 >= kNumCus) {
         const bool ta = op_t(transA), tb = op_t(transB);
         // Big tiles (one workgroup per CU) lose to 128 x 128 (two per CU)
@@ -478,7 +477,16 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // short there and 128 x 128 spreads unevenly (1072 x 2768 x 764 NT: 43.8
     // us against 54.3 for stream-K; 1536 x 2048 x 512: 57% of peak vs 49% for
     // 128 x 128).
-    if (t128 < 230 && kt < 32 && t64 >= 2 * kNumCus) return kCfg16x64;
+    // Below 230 tiles of 128 x 128, where the plain 64 x 64 tile is picked,
+    // 128 x 128 instead when its grid spreads nearly as evenly (at least 0.9
+    // of the 64 x 64 tile's balance x filled^3): 3-7% faster there (NN
+    // 1280 x 2560 x 512 5.1%, 1972 x 1644 x 788 6.8%; nine regret scans, mean
+    // regret 0.72% -> 0.67%), where at 0.875 (t128 >= 400, K = 512) 64 x 64
+    // still led by 6%.
+    auto plain64 = [&]() {
+        return cu_balance(t128) * fill3(128) >= 0.9 * cu_balance(t64) * fill3(64) ? cfg128 : kCfg16x64;
+    };
+    if (t128 < 230 && kt < 32 && t64 >= 2 * kNumCus) return plain64();
     // 461..511 tiles of 64 x 64 fill two k-group workgroups per CU to 90% or
     // more, which beats stream-K (1844 x 1056 x 2032 NN: 73.3 us against 81.6;
     // 828 x 2392 x 3588 NT: 7.9% faster).
@@ -493,7 +501,7 @@ int select_config(char transA, char transB, int M, int N, int K) {
     // or split-K over 64 x 64 tiles (1536 x 768 x 4096 TN: 71% of peak vs 63%;
     // 1024 x 1280 x 4096 NT: 73% vs 70%).
     if (t128 >= 72 && kt >= 64) return sk_or_split();
-    if (t64 >= 2 * kNumCus) return kCfg16x64;
+    if (t64 >= 2 * kNumCus) return plain64();
     // 257..511 tiles of 64 x 64 that fill 75-85% of two workgroup slots per
     // CU, with enough k-work and B not transposed: stream-K over 128 x 128
     // tiles keeps every CU busy for the whole k-range (NN 1280^3, beta 0.5:

@@ -271,7 +271,11 @@ def test_shape_class_selection():
     assert sel("N", "N", 1024, 2048, 512) == "mfma16_64x64x32_w2x2"
     assert sel("N", "N", 1344, 1408, 512) == "mfma16_64x64x32_w2x2_kg2"
     assert sel("N", "N", 1280, 1472, 512) == "mfma16_64x64x32_w2x2_kg2"
-    # ... and short k on up to 229 such tiles: the plain 64 x 64 tile.
+    # ... and short k on up to 229 such tiles: the plain 64 x 64 tile, or
+    # 128 x 128 where its grid spreads nearly as evenly.
+    assert sel("N", "N", 1280, 2560, 512) == "mfma16_128x128x32_w4x2"
+    assert sel("N", "N", 1972, 1644, 788) == "mfma16_128x128x32_w4x2"
+    assert sel("T", "T", 2560, 2560, 512) == "mfma16_64x64x32_w2x2"
     assert sel("N", "T", 1072, 2768, 764) == "mfma16_64x64x32_w2x2"
     assert sel("N", "N", 1536, 2048, 512) == "mfma16_64x64x32_w2x2"
     assert sel("N", "T", 2304, 2304, 1024) == "mfma32_128x128x32_w4x2_streamk_2wg"
